@@ -1,0 +1,329 @@
+"""CPU oracle for the routed-expert MoE forward layer.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module. The product
+path (the HIP library and its Python binding) never does, and this module never
+imports the product package: the two share no code.
+
+What it computes is the plain definition of a capacity-limited top-K MoE layer
+with rowwise dispatch, as the pages describe it:
+
+  * Olmo-core MoE report, Sec. 05 "Expert Parallelism": Fig. 15 (router ids and
+    weights of the two-rank example), Sec. 5.4 "Rowwise EP Removes Block Packing"
+    and Fig. 16 (route map: destination rank and row, negatives for invalid or
+    dropped routes, row = offset of the expert on its rank + earlier accepted
+    routes for that expert), Sec. 5.6 Table 8 (dispatch PUT / combine GET and
+    weighted reduce), Sec. 5.7 (packed prefix, unwritten tail).
+  * Olmo-core MoE report, Sec. 08 "Synchronization-Free Training", Sec. 8.5
+    (device cumulative offsets for grouped GEMM, tail-aware SwiGLU).
+  * AWS Neuron vLLM "Expert Parallelism (EP)" design: contiguous expert-to-rank
+    placement, every rank sees all tokens, partial sums over ranks add up to
+    the full combine (GPT-OSS-20B case study, "Why a single all-reduce works").
+
+Arithmetic is float64; values are rounded once to the layer's storage type at
+the points where the layer stores them (routing weights -> fp32; expert hidden
+activations H and expert outputs Y -> layer dtype; combined output -> layer
+dtype). Loops are used wherever order matters; library primitives (a stable
+sort, a matmul) serve as single steps.
+
+Readings of points the pages leave open (each is listed with its reason in the
+design notes of the repository):
+  * gating: softmax over the K selected logits (every printed weight set sums
+    to one and is in descending order);
+  * ties in top-K: lower expert id first; -0.0 equals +0.0;
+  * capacity is per expert, C = ceil(T*K*cf/N); the first C routes of an expert
+    in token order are kept, later ones dropped -- this admission order is
+    PARITY UNPINNED by the pages (the drawing's single drop cannot come from
+    any per-expert token-order rule); it is pinned only by brute force of the
+    stated rule;
+  * gate/up split of W_gu: rows [0, F) gate, rows [F, 2F) up -- PARITY UNPINNED
+    by the pages (the pages give the fused [H, 2I] shape only); pinned by
+    closed forms of the stated convention;
+  * weights of dropped routes are not renormalised (a dropped route adds zero).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "round_bf16", "round_to", "topk_softmax", "route_map", "dispatch_rows",
+    "silu", "expert_ffn", "expert_ffn_rows", "combine", "combine_tokens",
+    "moe_layer", "local_offsets",
+]
+
+
+# --------------------------------------------------------------------------
+# Rounding to storage types
+# --------------------------------------------------------------------------
+def round_bf16(v) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits and the fp32 exponent range. Written from
+    that definition: the quantum of a value with binary exponent e (v = m*2^e,
+    0.5 <= |m| < 1) is 2^(e-8), but never below 2^-133 (the subnormal spacing).
+    Values beyond the largest finite bfloat16 become +-inf. Returned as float64.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    out = np.array(v, copy=True)
+    finite = np.isfinite(v) & (v != 0)
+    if np.any(finite):
+        _, e = np.frexp(v[finite])
+        q = np.ldexp(1.0, np.maximum(e - 8, -133))
+        r = np.rint(v[finite] / q) * q          # rint = round half to even
+        bf16_max = (2.0 - 2.0 ** -7) * 2.0 ** 127
+        r = np.where(np.abs(r) > bf16_max, np.sign(r) * np.inf, r)
+        out[finite] = r
+    return out
+
+
+def round_to(v, dtype: str) -> np.ndarray:
+    """Round float64 values to the storage type ("f32" or "bf16"); float64 result."""
+    if dtype == "f32":
+        return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return round_bf16(v)
+    raise ValueError(dtype)
+
+
+# --------------------------------------------------------------------------
+# a1: top-K gating
+# --------------------------------------------------------------------------
+def topk_softmax(logits: np.ndarray, K: int):
+    """Top-K expert ids per token and their softmax weights.
+
+    Olmo-core MoE report, Sec. 05, Fig. 15: the router gives each token K expert
+    indices and K weights; every printed weight set is in descending order and
+    sums to one. Selection: experts ordered by (logit descending, id ascending),
+    the first K kept (a stable sort of -logit; IEEE comparison makes -0.0 and
+    +0.0 equal, so such ties fall back to the id). Weights: with m the largest
+    selected logit, w_k = exp(l_k - m) / sum_j exp(l_j - m) over the K selected
+    logits, evaluated in float64 and rounded once to fp32.
+
+    Returns (idx [T,K] int32, w [T,K] float32).
+    """
+    L = np.asarray(logits, dtype=np.float32)
+    T, N = L.shape
+    if not (1 <= K <= N):
+        raise ValueError("need 1 <= K <= N")
+    order = np.argsort(-L, axis=1, kind="stable")
+    idx = order[:, :K].astype(np.int32)
+    sel = np.take_along_axis(L, idx.astype(np.int64), axis=1).astype(np.float64)
+    m = sel[:, :1]
+    e = np.exp(sel - m)
+    w = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+    return idx, w
+
+
+# --------------------------------------------------------------------------
+# a2: route metadata (counts, admission, offsets, route map)
+# --------------------------------------------------------------------------
+def route_map(idx: np.ndarray, N: int, ep_size: int, C: int, ep_rank: int = 0):
+    """Route-map builder for a capacity-limited, expert-sharded layer.
+
+    Olmo-core MoE report, Sec. 5.4 and Fig. 16: two [T, K] tensors give, for
+    every route, the destination rank and the destination row in that rank's
+    expert-capacity buffer; negative entries mark invalid or dropped routes.
+    The row is the offset of the expert on its rank plus the number of earlier
+    accepted routes for that expert, and the capacity decision is applied before
+    any movement. AWS Neuron EP design: rank r owns experts [r*E_L, (r+1)*E_L).
+
+    ``idx`` may hold -1 for an invalid route. Steps, in order:
+      1. walk the routes in token order (t ascending, then k) and give each
+         valid route its position p among the earlier routes of its expert;
+         counts[e] is the number of routes to e;
+      2. a route is kept iff p < C;
+      3. kept[e] = min(counts[e], C); for rank r, off[r][j] is the sum of kept
+         over local experts j' < j (j = 0..E_L);
+      4. kept route: dest_rank = e // E_L, dest_row = off[rank][e % E_L] + p;
+         dropped route: both -1, drop_mask = 1; invalid route: both -1,
+         drop_mask = 0;
+      5. row_src (for ``ep_rank``): row_src[dest_row] = t*K + k for kept local
+         routes, -1 on the rows after the packed prefix.
+
+    Returns a dict of numpy arrays.
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    T, K = idx.shape
+    if N % ep_size != 0:
+        raise ValueError("N must be a multiple of ep_size")
+    E_L = N // ep_size
+    counts = np.zeros(N, dtype=np.int64)
+    pos = np.full((T, K), -1, dtype=np.int64)
+    for t in range(T):
+        for k in range(K):
+            e = idx[t, k]
+            if e < 0:
+                continue
+            pos[t, k] = counts[e]
+            counts[e] += 1
+    kept = np.minimum(counts, C)
+    offsets = np.zeros((ep_size, E_L + 1), dtype=np.int64)
+    for r in range(ep_size):
+        for j in range(E_L):
+            offsets[r, j + 1] = offsets[r, j] + kept[r * E_L + j]
+    dest_rank = np.full((T, K), -1, dtype=np.int64)
+    dest_row = np.full((T, K), -1, dtype=np.int64)
+    drop_mask = np.zeros((T, K), dtype=np.uint8)
+    row_src = np.full(E_L * C, -1, dtype=np.int64)
+    for t in range(T):
+        for k in range(K):
+            e = idx[t, k]
+            if e < 0:
+                continue
+            if pos[t, k] >= C:
+                drop_mask[t, k] = 1
+                continue
+            r, j = divmod(int(e), E_L)
+            row = offsets[r, j] + pos[t, k]
+            dest_rank[t, k] = r
+            dest_row[t, k] = row
+            if r == ep_rank:
+                row_src[row] = t * K + k
+    return {
+        "counts": counts.astype(np.int32),
+        "offsets": offsets.astype(np.int32),
+        "dest_rank": dest_rank.astype(np.int32),
+        "dest_row": dest_row.astype(np.int32),
+        "drop_mask": drop_mask,
+        "row_src": row_src.astype(np.int32),
+        "pos": pos.astype(np.int32),
+    }
+
+
+def local_offsets(offsets: np.ndarray, ep_rank: int) -> np.ndarray:
+    """The cumulative row offsets [E_L+1] of rank ``ep_rank``'s local experts."""
+    return np.asarray(offsets)[ep_rank]
+
+
+# --------------------------------------------------------------------------
+# a3: rowwise dispatch
+# --------------------------------------------------------------------------
+def dispatch_rows(x: np.ndarray, dest_rank: np.ndarray, dest_row: np.ndarray,
+                  ep_rank: int, n_rows: int) -> np.ndarray:
+    """buf[dest_row[t,k]] = x[t] for every route whose dest_rank is ``ep_rank``.
+
+    Olmo-core MoE report, Sec. 5.6 Table 8 (dispatch forward: the token-source
+    rank pushes x_t to the capacity row assigned to the selected expert) and
+    the closing paragraph of Sec. 5.6 (PUT skips negative destinations). Rows
+    not written stay NaN here, so a reader of the tail is visible.
+    Returns buf [n_rows, d] with x's dtype (an exact copy, no arithmetic).
+    """
+    x = np.asarray(x)
+    buf = np.full((n_rows, x.shape[1]), np.nan, dtype=x.dtype)
+    T, K = dest_rank.shape
+    for t in range(T):
+        for k in range(K):
+            if dest_rank[t, k] == ep_rank and dest_row[t, k] >= 0:
+                buf[dest_row[t, k]] = x[t]
+    return buf
+
+
+# --------------------------------------------------------------------------
+# a4: grouped expert SwiGLU FFN over the packed prefix
+# --------------------------------------------------------------------------
+def silu(z):
+    """silu(z) = z / (1 + exp(-z)) (float64)."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn_rows(X: np.ndarray, w_gu_j: np.ndarray, w_d_j: np.ndarray, dtype: str):
+    """Bias-free SwiGLU MLP of one expert on rows X.
+
+    Olmo-core MoE report, Sec. 5.2 and Fig. 14 (Linear 1 -> SwiGLU -> Linear 2)
+    and Sec. 04 "Distributed Data Parallel" (bias-free SwiGLU expert MLP).
+    With W_gu[j] of shape [2F, d] (rows [0,F) gate, [F,2F) up) and W_d[j] of
+    shape [d, F]: G = X W_gate^T, U = X W_up^T, H = silu(G) * U rounded to the
+    storage type, Y = H W_d^T rounded to the storage type.
+    Returns (H, Y) as float64 arrays holding storage-type values.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(w_gu_j, dtype=np.float64)
+    F = W.shape[0] // 2
+    G = X @ W[:F].T
+    U = X @ W[F:].T
+    H = round_to(silu(G) * U, dtype)
+    Y = round_to(H @ np.asarray(w_d_j, dtype=np.float64).T, dtype)
+    return H, Y
+
+
+def expert_ffn(buf: np.ndarray, offsets_local: np.ndarray, w_gu: np.ndarray,
+               w_d: np.ndarray, dtype: str):
+    """Grouped expert FFN over each local expert's row interval.
+
+    Olmo-core MoE report, Sec. 5.7 (the local experts' rows are packed back to
+    back from row 0, one unwritten tail follows; grouped GEMM skips the tail)
+    and Sec. 08 Sec. 8.5 (int32 cumulative offsets; tail-aware SwiGLU). Expert
+    j owns rows [off[j], off[j+1]). Rows after off[E_L] are left NaN.
+    Returns (H [rows, F], Y [rows, d]) float64.
+    """
+    E_L = len(offsets_local) - 1
+    rows = buf.shape[0]
+    F = w_gu.shape[1] // 2
+    d = w_d.shape[1]
+    H = np.full((rows, F), np.nan)
+    Y = np.full((rows, d), np.nan)
+    for j in range(E_L):
+        a, b = int(offsets_local[j]), int(offsets_local[j + 1])
+        if b > a:
+            H[a:b], Y[a:b] = expert_ffn_rows(buf[a:b], w_gu[j], w_d[j], dtype)
+    return H, Y
+
+
+# --------------------------------------------------------------------------
+# a5: weighted combine back to token order
+# --------------------------------------------------------------------------
+def combine_tokens(tokens, y_of_row, dest_rank, dest_row, w, ep_rank: int, d: int,
+                   dtype: str) -> np.ndarray:
+    """Combine for a subset of tokens; ``y_of_row(row)`` returns that expert row.
+
+    Olmo-core MoE report, Sec. 5.6 Table 8 (combine forward: the token source
+    pulls the selected expert outputs and performs the router-weighted
+    reduction) and its closing paragraph (invalid entries gather zero).
+    AWS Neuron EP design: a rank contributes only its local experts' outputs,
+    tokens not routed to it get zero. out[t] = sum over k ascending with
+    dest_rank[t,k] == ep_rank of w[t,k] * y[dest_row[t,k]], in float64,
+    rounded once to the storage type.
+    """
+    out = np.zeros((len(tokens), d), dtype=np.float64)
+    K = dest_rank.shape[1]
+    for i, t in enumerate(tokens):
+        acc = np.zeros(d, dtype=np.float64)
+        for k in range(K):
+            if dest_rank[t, k] == ep_rank and dest_row[t, k] >= 0:
+                acc += float(w[t, k]) * np.asarray(y_of_row(int(dest_row[t, k])), dtype=np.float64)
+        out[i] = acc
+    return round_to(out, dtype)
+
+
+def combine(y: np.ndarray, dest_rank, dest_row, w, ep_rank: int, dtype: str) -> np.ndarray:
+    """Combine for all tokens (see ``combine_tokens``). Returns [T, d] float64."""
+    T = dest_rank.shape[0]
+    y = np.asarray(y)
+    return combine_tokens(range(T), lambda r: y[r], dest_rank, dest_row, w, ep_rank,
+                          y.shape[1], dtype)
+
+
+# --------------------------------------------------------------------------
+# Whole layer
+# --------------------------------------------------------------------------
+def moe_layer(logits, x, w_gu, w_d, K: int, C: int, ep_size: int, ep_rank: int, dtype: str):
+    """Route -> dispatch -> grouped SwiGLU FFN -> combine, for one rank's shard.
+
+    The step order of the rowwise path in Olmo-core MoE report Sec. 05 Fig. 16:
+    route-map build, row dispatch, grouped expert computation, row gather and
+    weighted reduce. Returns a dict with every intermediate.
+    """
+    logits = np.asarray(logits, dtype=np.float32)
+    N = logits.shape[1]
+    idx, w = topk_softmax(logits, K)
+    rm = route_map(idx, N, ep_size, C, ep_rank)
+    E_L = N // ep_size
+    buf = dispatch_rows(np.asarray(x, dtype=np.float64), rm["dest_rank"], rm["dest_row"],
+                        ep_rank, E_L * C)
+    H, Y = expert_ffn(buf, rm["offsets"][ep_rank], w_gu, w_d, dtype)
+    out = combine(Y, rm["dest_rank"], rm["dest_row"], w, ep_rank, dtype)
+    res = dict(rm)
+    res.update(topk_idx=idx, topk_w=w, buf=buf, h=H, y=Y, out=out)
+    return res
