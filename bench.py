@@ -1,0 +1,197 @@
+"""Benchmark of the routed-expert MoE forward layer on one MI355X.
+
+A step is one pass of the whole layer (route -> dispatch -> expert up (GEMM +
+SwiGLU) -> expert down -> combine) over one batch of seeded synthetic input
+already resident in HBM. Default workload: the OLMoE-shaped bf16 layer
+(T=8192, d=2048, 64 experts, top-8, F=1024, capacity factor 1.25).
+
+Prints one JSON line. ``value`` is routed token-rows per second (kept routes
+to this GPU's experts per layer forward / layer time). Stage times come from
+HIP events recorded between the calls on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16: 256 CU x 2.4 GHz x 4096 flop/clk
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, published
+STAGES = ["route", "dispatch", "up", "down", "combine"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="olmoe_bf16")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def cpu_baseline(cfg, target_s: float) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload: a
+    T_s-token layer of the same shape drawn with the same recipe (capacity
+    recomputed for T_s), sized to take about ``target_s`` seconds."""
+    import threadpoolctl
+
+    from combine_top_softmax_amd.workloads import make_inputs
+    from oracle import moe_oracle as orc
+
+    def run(T_s):
+        c = cfg.with_(T=T_s)
+        inp = make_inputs(c, "cpu")
+        args = (inp.logits.numpy(), inp.x.double().numpy(), inp.w_gu.double().numpy(),
+                inp.w_d.double().numpy(), c.K, c.capacity, c.ep_size, c.ep_rank, c.dtype)
+        t0 = time.perf_counter()
+        ref = orc.moe_layer(*args)
+        dt = time.perf_counter() - t0
+        return int(ref["offsets"][c.ep_rank, -1]), dt
+
+    T_s = min(cfg.T, 256)
+    rows, dt = run(T_s)
+    if dt < target_s / 3 and T_s < cfg.T:
+        T_s = min(cfg.T, max(T_s + 1, int(T_s * target_s / max(dt, 1e-3))))
+        rows, dt = run(T_s)
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
+    return {"value": rows / dt, "unit": "token-rows/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole layer (route, dispatch, FFN, combine) on a {T_s}-token layer of "
+                      f"the {cfg.name} shape, same input recipe, capacity recomputed for {T_s} "
+                      f"tokens: {rows} routed rows in {dt:.2f} s; NumPy float64, "
+                      f"BLAS threads={threads}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the expert-parallel exchange across GPUs is not part of it)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import combine_top_softmax_amd as moe
+    from combine_top_softmax_amd.workloads import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.workload]
+    shape = moe.MoeShape.from_config(cfg)
+    inp = make_inputs(cfg, "cuda")
+    layer = moe.MoELayer(shape, "cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        layer.route_step(inp.logits)
+        if ev: ev[1].record(stream)
+        layer.dispatch_step(inp.x)
+        if ev: ev[2].record(stream)
+        layer.up_step(inp.w_gu)
+        if ev: ev[3].record(stream)
+        layer.down_step(inp.w_d)
+        if ev: ev[4].record(stream)
+        layer.combine_step()
+        if ev: ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.set_sync_debug_mode("error")      # any host sync in the loop raises
+    t_host0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    t_host = time.perf_counter() - t_host0
+    torch.cuda.set_sync_debug_mode(0)
+    torch.cuda.synchronize()
+
+    total_ms = evs[0][0].elapsed_time(evs[-1][5])
+    ms_step = total_ms / args.steps
+    stage_ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+                for i, name in enumerate(STAGES)}
+
+    # workload actually routed (read after the timed loop)
+    R = int(layer.route.offsets[cfg.ep_rank, -1].item())
+    local = layer.route.dest_rank == cfg.ep_rank
+    S = int(local.any(dim=1).sum().item())
+    drops = int(layer.route.drop_mask.sum().item())
+    e = cfg.elem_bytes
+    T, d, N, K, F = cfg.T, cfg.d, cfg.N, cfg.K, cfg.F
+    bytes_ = {
+        "route": 4 * T * N + 17 * T * K,
+        "dispatch": (S + R) * d * e + 8 * T * K,
+        "combine": (R + T) * d * e + 12 * T * K,
+    }
+    flops = {"up": 4.0 * R * d * F, "down": 2.0 * R * d * F}
+    stages = {}
+    for name in STAGES:
+        t = stage_ms[name] * 1e-3
+        st = {"ms": round(stage_ms[name], 5)}
+        if name in bytes_:
+            st["GBps"] = round(bytes_[name] / t / 1e9, 1)
+            st["hbm_frac"] = round(bytes_[name] / t / 1e9 / HBM_PEAK_GBPS, 4)
+        if name in flops:
+            st["TFLOPs"] = round(flops[name] / t / 1e12, 1)
+            st["mfma_frac"] = round(flops[name] / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        stages[name] = st
+    dc_bytes = bytes_["dispatch"] + bytes_["combine"]
+    dc_t = (stage_ms["dispatch"] + stage_ms["combine"]) * 1e-3
+    ffn_t = (stage_ms["up"] + stage_ms["down"]) * 1e-3
+    dominant = max(STAGES, key=lambda n: stage_ms[n])
+    if dominant in flops and cfg.dtype == "bf16":
+        ach = flops[dominant] / (stage_ms[dominant] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None, "kernel": dominant}
+    elif dominant in flops:
+        ach = flops[dominant] / (stage_ms[dominant] * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(ach, 3), "peak": FP32_VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / FP32_VALU_PEAK_TFLOPS, 5),
+                "traffic": None, "kernel": dominant}
+    else:
+        ach = bytes_[dominant] / (stage_ms[dominant] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dominant}
+
+    result = {
+        "metric": "routed token-rows/sec per MoE layer fwd; dispatch+combine HBM GB/s; GEMM MFMA %",
+        "value": round(R / (ms_step * 1e-3), 1),
+        "unit": "token-rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded torch generator on the device; N(0,1) logits and x, "
+                "N(0,0.02^2) expert weights)",
+        "config": {"workload": cfg.name, "T": T, "d": d, "N": N, "K": K, "F": F,
+                   "cf": str(cfg.cf), "capacity": cfg.capacity, "ep_size": cfg.ep_size,
+                   "ep_rank": cfg.ep_rank, "parallelism": "single GPU, all local experts"
+                   if cfg.ep_size == 1 else f"one expert shard of {cfg.ep_size}"},
+        "routed_rows": R, "source_tokens": S, "dropped_routes": drops,
+        "dispatch_combine_GBps": round(dc_bytes / dc_t / 1e9, 1),
+        "dispatch_combine_hbm_frac": round(dc_bytes / dc_t / 1e9 / HBM_PEAK_GBPS, 4),
+        "gemm_TFLOPs": round(6.0 * R * d * F / ffn_t / 1e12, 1),
+        "gemm_mfma_frac": round(6.0 * R * d * F / ffn_t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "host_enqueue_ms_per_step": round(t_host * 1e3 / args.steps, 4),
+        "stages": stages,
+        "roofline": roof,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_seconds),
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,275 @@
+"""MI355X-native routed-expert MoE forward layer: thin Python binding.
+
+Every step of the layer runs in the HIP library ``libmoe_hip.so`` (C ABI in
+``include/moe.h``); this module only checks tensor shapes on the host and
+passes device pointers and the current HIP stream. There is no CPU fallback:
+if the library is missing, every call raises.
+
+    shape = MoeShape.from_config(cfg)
+    layer = MoELayer(shape, device="cuda")      # buffers allocated once
+    out = layer.forward(logits, x, w_gu, w_d)   # 4 calls, no host sync
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _abi
+from ._abi import MoeError  # noqa: F401
+
+__all__ = [
+    "MoeShape", "RouteOut", "MoELayer", "MoeError", "moe_route_workspace_size", "moe_route",
+    "moe_route_map", "moe_dispatch_rows", "moe_expert_ffn", "moe_expert_up",
+    "moe_expert_down", "moe_combine", "moe_strerror", "moe_validate_shape",
+]
+
+
+@dataclass(frozen=True)
+class MoeShape:
+    T: int
+    d: int
+    N: int
+    K: int
+    F: int
+    ep_size: int
+    ep_rank: int
+    capacity: int
+    dtype: str  # "f32" | "bf16"
+
+    @classmethod
+    def from_config(cls, cfg) -> "MoeShape":
+        return cls(cfg.T, cfg.d, cfg.N, cfg.K, cfg.F, cfg.ep_size, cfg.ep_rank,
+                   cfg.capacity, cfg.dtype)
+
+    @property
+    def E_L(self) -> int:
+        return self.N // self.ep_size
+
+    @property
+    def rows(self) -> int:
+        return self.E_L * self.capacity
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def c(self) -> _abi.moe_shape_t:
+        if self.dtype not in ("f32", "bf16"):
+            raise ValueError(f"dtype must be 'f32' or 'bf16', got {self.dtype!r}")
+        return _abi.moe_shape_t(self.T, self.d, self.N, self.K, self.F, self.ep_size,
+                                self.ep_rank, self.capacity,
+                                _abi.MOE_F32 if self.dtype == "f32" else _abi.MOE_BF16)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, shape: tuple, dtype: torch.dtype) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class RouteOut:
+    topk_idx: torch.Tensor   # [T,K] int32
+    topk_w: torch.Tensor     # [T,K] fp32
+    dest_rank: torch.Tensor  # [T,K] int32
+    dest_row: torch.Tensor   # [T,K] int32
+    drop_mask: torch.Tensor  # [T,K] uint8
+    counts: torch.Tensor     # [N] int32
+    offsets: torch.Tensor    # [ep_size, E_L+1] int32
+    row_src: torch.Tensor | None  # [E_L*C] int32
+
+    @classmethod
+    def empty(cls, shape: MoeShape, device="cuda", row_src: bool = True) -> "RouteOut":
+        T, K = shape.T, shape.K
+        i32 = dict(dtype=torch.int32, device=device)
+        return cls(torch.empty(T, K, **i32), torch.empty(T, K, dtype=torch.float32, device=device),
+                   torch.empty(T, K, **i32), torch.empty(T, K, **i32),
+                   torch.empty(T, K, dtype=torch.uint8, device=device),
+                   torch.empty(shape.N, **i32), torch.empty(shape.ep_size, shape.E_L + 1, **i32),
+                   torch.empty(shape.rows, **i32) if row_src else None)
+
+    def check(self, shape: MoeShape, need_topk: bool = True) -> None:
+        T, K = shape.T, shape.K
+        if need_topk:
+            _need(self.topk_idx, "topk_idx", (T, K), torch.int32)
+            _need(self.topk_w, "topk_w", (T, K), torch.float32)
+        _need(self.dest_rank, "dest_rank", (T, K), torch.int32)
+        _need(self.dest_row, "dest_row", (T, K), torch.int32)
+        _need(self.drop_mask, "drop_mask", (T, K), torch.uint8)
+        _need(self.counts, "counts", (shape.N,), torch.int32)
+        _need(self.offsets, "offsets", (shape.ep_size, shape.E_L + 1), torch.int32)
+        if self.row_src is not None:
+            _need(self.row_src, "row_src", (shape.rows,), torch.int32)
+
+    def c(self, need_topk: bool = True) -> _abi.moe_route_out_t:
+        return _abi.moe_route_out_t(
+            self.topk_idx.data_ptr() if need_topk else None,
+            self.topk_w.data_ptr() if need_topk else None,
+            self.dest_rank.data_ptr(), self.dest_row.data_ptr(), self.drop_mask.data_ptr(),
+            self.counts.data_ptr(), self.offsets.data_ptr(),
+            None if self.row_src is None else self.row_src.data_ptr())
+
+
+# ----------------------------------------------------------------- C ABI calls
+def moe_strerror(code: int) -> str:
+    return _abi.load().moe_strerror(code).decode()
+
+
+def moe_validate_shape(shape: MoeShape) -> int:
+    return _abi.load().moe_validate_shape(ctypes.byref(shape.c()))
+
+
+def moe_route_workspace_size(shape: MoeShape) -> int:
+    n = ctypes.c_size_t(0)
+    _abi.check("moe_route_workspace_size",
+               _abi.load().moe_route_workspace_size(ctypes.byref(shape.c()), ctypes.byref(n)))
+    return n.value
+
+
+def _ws_check(ws: torch.Tensor, shape: MoeShape) -> None:
+    need = moe_route_workspace_size(shape)
+    if ws.device.type != "cuda" or ws.numel() * ws.element_size() < need or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous device tensor of >= {need} bytes")
+
+
+def moe_route(shape: MoeShape, logits: torch.Tensor, out: RouteOut, ws: torch.Tensor,
+              stream=None) -> None:
+    _need(logits, "logits", (shape.T, shape.N), torch.float32)
+    out.check(shape)
+    _ws_check(ws, shape)
+    rc = _abi.load().moe_route(ctypes.byref(shape.c()), _ptr(logits), ctypes.byref(out.c()),
+                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _abi.check("moe_route", rc)
+
+
+def moe_route_map(shape: MoeShape, topk_idx_in: torch.Tensor, out: RouteOut, ws: torch.Tensor,
+                  stream=None) -> None:
+    _need(topk_idx_in, "topk_idx_in", (shape.T, shape.K), torch.int32)
+    out.check(shape, need_topk=False)
+    _ws_check(ws, shape)
+    rc = _abi.load().moe_route_map(ctypes.byref(shape.c()), _ptr(topk_idx_in),
+                                   ctypes.byref(out.c(need_topk=False)), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream))
+    _abi.check("moe_route_map", rc)
+
+
+def moe_dispatch_rows(shape: MoeShape, x, dest_rank, dest_row, buf, stream=None) -> None:
+    dt = shape.torch_dtype
+    _need(x, "x", (shape.T, shape.d), dt)
+    _need(dest_rank, "dest_rank", (shape.T, shape.K), torch.int32)
+    _need(dest_row, "dest_row", (shape.T, shape.K), torch.int32)
+    _need(buf, "buf", (shape.rows, shape.d), dt)
+    rc = _abi.load().moe_dispatch_rows(ctypes.byref(shape.c()), _ptr(x), _ptr(dest_rank),
+                                       _ptr(dest_row), _ptr(buf), _stream(stream))
+    _abi.check("moe_dispatch_rows", rc)
+
+
+def _ffn_checks(shape, offsets):
+    _need(offsets, "offsets", (shape.ep_size, shape.E_L + 1), torch.int32)
+
+
+def moe_expert_up(shape: MoeShape, buf, offsets, w_gu, h, stream=None) -> None:
+    dt = shape.torch_dtype
+    _need(buf, "buf", (shape.rows, shape.d), dt)
+    _ffn_checks(shape, offsets)
+    _need(w_gu, "w_gu", (shape.E_L, 2 * shape.F, shape.d), dt)
+    _need(h, "h", (shape.rows, shape.F), dt)
+    rc = _abi.load().moe_expert_up(ctypes.byref(shape.c()), _ptr(buf), _ptr(offsets),
+                                   _ptr(w_gu), _ptr(h), _stream(stream))
+    _abi.check("moe_expert_up", rc)
+
+
+def moe_expert_down(shape: MoeShape, h, offsets, w_down, y, stream=None) -> None:
+    dt = shape.torch_dtype
+    _need(h, "h", (shape.rows, shape.F), dt)
+    _ffn_checks(shape, offsets)
+    _need(w_down, "w_down", (shape.E_L, shape.d, shape.F), dt)
+    _need(y, "y", (shape.rows, shape.d), dt)
+    rc = _abi.load().moe_expert_down(ctypes.byref(shape.c()), _ptr(h), _ptr(offsets),
+                                     _ptr(w_down), _ptr(y), _stream(stream))
+    _abi.check("moe_expert_down", rc)
+
+
+def moe_expert_ffn(shape: MoeShape, buf, offsets, w_gu, w_down, h, y, stream=None) -> None:
+    dt = shape.torch_dtype
+    _need(buf, "buf", (shape.rows, shape.d), dt)
+    _ffn_checks(shape, offsets)
+    _need(w_gu, "w_gu", (shape.E_L, 2 * shape.F, shape.d), dt)
+    _need(w_down, "w_down", (shape.E_L, shape.d, shape.F), dt)
+    _need(h, "h", (shape.rows, shape.F), dt)
+    _need(y, "y", (shape.rows, shape.d), dt)
+    rc = _abi.load().moe_expert_ffn(ctypes.byref(shape.c()), _ptr(buf), _ptr(offsets),
+                                    _ptr(w_gu), _ptr(w_down), _ptr(h), _ptr(y), _stream(stream))
+    _abi.check("moe_expert_ffn", rc)
+
+
+def moe_combine(shape: MoeShape, y, dest_rank, dest_row, topk_w, out, stream=None) -> None:
+    dt = shape.torch_dtype
+    _need(y, "y", (shape.rows, shape.d), dt)
+    _need(dest_rank, "dest_rank", (shape.T, shape.K), torch.int32)
+    _need(dest_row, "dest_row", (shape.T, shape.K), torch.int32)
+    _need(topk_w, "topk_w", (shape.T, shape.K), torch.float32)
+    _need(out, "out", (shape.T, shape.d), dt)
+    rc = _abi.load().moe_combine(ctypes.byref(shape.c()), _ptr(y), _ptr(dest_rank),
+                                 _ptr(dest_row), _ptr(topk_w), _ptr(out), _stream(stream))
+    _abi.check("moe_combine", rc)
+
+
+# ----------------------------------------------------------------- layer
+class MoELayer:
+    """Capacity-shaped buffers allocated once; ``forward`` enqueues the four
+    calls back to back on the current stream with no host synchronization."""
+
+    def __init__(self, shape: MoeShape, device="cuda", row_src: bool = True):
+        _abi.load()
+        self.shape = shape
+        dt = shape.torch_dtype
+        self.route = RouteOut.empty(shape, device, row_src=row_src)
+        self.ws = torch.empty(moe_route_workspace_size(shape), dtype=torch.uint8, device=device)
+        self.buf = torch.empty(shape.rows, shape.d, dtype=dt, device=device)
+        self.h = torch.empty(shape.rows, shape.F, dtype=dt, device=device)
+        self.y = torch.empty(shape.rows, shape.d, dtype=dt, device=device)
+        self.out = torch.empty(shape.T, shape.d, dtype=dt, device=device)
+
+    def route_step(self, logits, stream=None):
+        moe_route(self.shape, logits, self.route, self.ws, stream)
+
+    def dispatch_step(self, x, stream=None):
+        r = self.route
+        moe_dispatch_rows(self.shape, x, r.dest_rank, r.dest_row, self.buf, stream)
+
+    def up_step(self, w_gu, stream=None):
+        moe_expert_up(self.shape, self.buf, self.route.offsets, w_gu, self.h, stream)
+
+    def down_step(self, w_d, stream=None):
+        moe_expert_down(self.shape, self.h, self.route.offsets, w_d, self.y, stream)
+
+    def combine_step(self, stream=None):
+        r = self.route
+        moe_combine(self.shape, self.y, r.dest_rank, r.dest_row, r.topk_w, self.out, stream)
+
+    def forward(self, logits, x, w_gu, w_d, stream=None) -> torch.Tensor:
+        self.route_step(logits, stream)
+        self.dispatch_step(x, stream)
+        moe_expert_ffn(self.shape, self.buf, self.route.offsets, w_gu, w_d, self.h, self.y,
+                       stream)
+        self.combine_step(stream)
+        return self.out

@@ -1,0 +1,142 @@
+// C ABI entry points of libmoe_hip (declared in include/moe.h).
+//
+// Host-only validation, then stream-ordered kernel launches. Nothing here
+// reads device memory, synchronizes or allocates (Olmo-core MoE report,
+// Sec. 08 "Synchronization-Free Training", Sec. 8.5: device-resident route
+// metadata, capacity-shaped buffers fixed before the loop).
+#include "moe_internal.h"
+
+namespace {
+
+using moe::ceil_div;
+
+bool aligned16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool aligned4(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+int check_shape(const moe_shape_t *s) {
+  if (s == nullptr) return MOE_EINVAL;
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_EDTYPE;
+  if (s->T < 1 || s->d < 1 || s->N < 1 || s->K < 1 || s->F < 1 || s->ep_size < 1 ||
+      s->capacity < 1)
+    return MOE_EINVAL;
+  if (s->K > s->N || s->K > MOE_MAX_K || s->N > MOE_MAX_EXPERTS) return MOE_EINVAL;
+  if (s->N % s->ep_size != 0 || s->ep_rank < 0 || s->ep_rank >= s->ep_size) return MOE_EINVAL;
+  if (s->d % 8 != 0 || s->F % 8 != 0) return MOE_EINVAL;
+  const int64_t E_L = s->N / s->ep_size;
+  if ((int64_t)s->T * s->K >= (int64_t)1 << 31) return MOE_EINVAL;
+  if (E_L * s->capacity >= (int64_t)1 << 31) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+size_t route_ws_bytes(const moe_shape_t &s) {
+  const size_t hist = (size_t)s.N * moe::route_tiles(s) * sizeof(int32_t);
+  const size_t rank = (size_t)s.T * s.K;
+  return ((hist + rank) + 255) / 256 * 256;
+}
+
+int check_route_out(const moe_shape_t &s, const moe_route_out_t *o, bool need_topk) {
+  if (o == nullptr) return MOE_EINVAL;
+  if (need_topk && (!aligned4(o->topk_idx) || !aligned4(o->topk_w))) return MOE_EALIGN;
+  if (!aligned4(o->dest_rank) || !aligned4(o->dest_row) || o->drop_mask == nullptr ||
+      !aligned4(o->counts) || !aligned4(o->offsets))
+    return MOE_EALIGN;
+  if (o->row_src != nullptr && !aligned4(o->row_src)) return MOE_EALIGN;
+  (void)s;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_validate_shape(const moe_shape_t *shape) { return check_shape(shape); }
+
+const char *moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "success";
+    case MOE_EINVAL: return "invalid size or index argument";
+    case MOE_EDTYPE: return "unknown dtype";
+    case MOE_EALIGN: return "data pointer is NULL or misaligned (16 bytes for rows, 4 for int32/fp32 arrays)";
+    case MOE_EWORKSPACE: return "workspace is NULL or smaller than moe_route_workspace_size";
+    case MOE_EHIP: return "HIP kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+int moe_route_workspace_size(const moe_shape_t *shape, size_t *bytes) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (bytes == nullptr) return MOE_EINVAL;
+  *bytes = route_ws_bytes(*shape);
+  return MOE_OK;
+}
+
+int moe_route(const moe_shape_t *shape, const float *logits, const moe_route_out_t *out,
+              void *ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!aligned16(logits)) return MOE_EALIGN;
+  if ((rc = check_route_out(*shape, out, true)) != MOE_OK) return rc;
+  if (!aligned4(ws) || ws_bytes < route_ws_bytes(*shape)) return MOE_EWORKSPACE;
+  return moe::launch_route(*shape, logits, nullptr, *out, ws, stream);
+}
+
+int moe_route_map(const moe_shape_t *shape, const int32_t *topk_idx_in,
+                  const moe_route_out_t *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!aligned4(topk_idx_in)) return MOE_EALIGN;
+  if ((rc = check_route_out(*shape, out, false)) != MOE_OK) return rc;
+  if (!aligned4(ws) || ws_bytes < route_ws_bytes(*shape)) return MOE_EWORKSPACE;
+  return moe::launch_route(*shape, nullptr, topk_idx_in, *out, ws, stream);
+}
+
+int moe_dispatch_rows(const moe_shape_t *shape, const void *x, const int32_t *dest_rank,
+                      const int32_t *dest_row, void *buf, hipStream_t stream) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!aligned16(x) || !aligned16(buf) || !aligned4(dest_rank) || !aligned4(dest_row))
+    return MOE_EALIGN;
+  return moe::launch_dispatch(*shape, x, dest_rank, dest_row, buf, stream);
+}
+
+int moe_expert_up(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
+                  const void *w_gu, void *h, hipStream_t stream) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!aligned16(buf) || !aligned16(w_gu) || !aligned16(h) || !aligned4(offsets))
+    return MOE_EALIGN;
+  return moe::launch_expert_up(*shape, buf, offsets, w_gu, h, stream);
+}
+
+int moe_expert_down(const moe_shape_t *shape, const void *h, const int32_t *offsets,
+                    const void *w_down, void *y, hipStream_t stream) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!aligned16(h) || !aligned16(w_down) || !aligned16(y) || !aligned4(offsets))
+    return MOE_EALIGN;
+  return moe::launch_expert_down(*shape, h, offsets, w_down, y, stream);
+}
+
+int moe_expert_ffn(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
+                   const void *w_gu, const void *w_down, void *h, void *y, hipStream_t stream) {
+  int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!aligned16(buf) || !aligned16(w_gu) || !aligned16(w_down) || !aligned16(h) ||
+      !aligned16(y) || !aligned4(offsets))
+    return MOE_EALIGN;
+  if ((rc = moe::launch_expert_up(*shape, buf, offsets, w_gu, h, stream)) != MOE_OK) return rc;
+  return moe::launch_expert_down(*shape, h, offsets, w_down, y, stream);
+}
+
+int moe_combine(const moe_shape_t *shape, const void *y, const int32_t *dest_rank,
+                const int32_t *dest_row, const float *topk_w, void *out, hipStream_t stream) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!aligned16(y) || !aligned16(out) || !aligned4(dest_rank) || !aligned4(dest_row) ||
+      !aligned4(topk_w))
+    return MOE_EALIGN;
+  return moe::launch_combine(*shape, y, dest_rank, dest_row, topk_w, out, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal declarations shared by the HIP translation units of libmoe_hip.
+// Not part of the public C ABI (include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kRouteTile = 64;     // tokens per routing tile (one wave, one lane per token)
+constexpr int kNumXcd = 8;         // MI355X: 8 accelerator complex dies, each with its own L2
+
+// ---- host-side helpers -----------------------------------------------------
+inline int elem_bytes(moe_dtype_t dt) { return dt == MOE_F32 ? 4 : 2; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int route_tiles(const moe_shape_t &s) { return (int)ceil_div(s.T, kRouteTile); }
+
+// Launchers (return MOE_OK or MOE_EHIP). Shapes are already validated.
+int launch_route(const moe_shape_t &s, const float *logits, const int32_t *ids_in,
+                 const moe_route_out_t &o, void *ws, hipStream_t st);
+int launch_dispatch(const moe_shape_t &s, const void *x, const int32_t *dest_rank,
+                    const int32_t *dest_row, void *buf, hipStream_t st);
+int launch_combine(const moe_shape_t &s, const void *y, const int32_t *dest_rank,
+                   const int32_t *dest_row, const float *w, void *out, hipStream_t st);
+int launch_expert_up(const moe_shape_t &s, const void *buf, const int32_t *offsets,
+                     const void *w_gu, void *h, hipStream_t st);
+int launch_expert_down(const moe_shape_t &s, const void *h, const int32_t *offsets,
+                       const void *w_d, void *y, hipStream_t st);
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// ---- device-side helpers ---------------------------------------------------
+// bfloat16 <-> float. The float -> bf16 conversion of __bf16 rounds to nearest
+// even (the gfx950 hardware conversion).
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Wave-wide inclusive prefix sum of an int (64 lanes).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,166 @@
+// Rowwise dispatch and weighted combine: HBM-bound row movement.
+//
+// Olmo-core MoE report, Sec. 05 "Expert Parallelism", Sec. 5.6 and Table 8:
+// dispatch forward pushes x_t into the capacity row of each selected expert
+// (one read of the source row, fan-out to up to K destinations; negative
+// destinations are skipped); combine forward gathers the K selected expert
+// rows of a token, multiplies them by the router weights and sums them in
+// token order (invalid entries gather zero).
+//
+// One wave per token row. A row is moved in 16-byte vectors (dwordx4), 64
+// lanes side by side, so every wave access is a contiguous 1 KiB segment.
+// Dispatch loads the source row once into registers and stores it to each
+// local destination. Combine accumulates in fp32, k ascending, and writes each
+// output row exactly once (no atomics, deterministic).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRowsPerBlock = 4;   // 4 waves = 4 token rows per 256-thread block
+
+// Segment of a row: up to 64*NV 16-byte vectors handled per pass.
+template <int NV>
+__global__ __launch_bounds__(256) void k_dispatch(
+    const u32x4_t *__restrict__ x, const int32_t *__restrict__ dest_rank,
+    const int32_t *__restrict__ dest_row, u32x4_t *__restrict__ buf, int T, int K,
+    int nvec, int ep_rank) {
+  const int lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6));
+  if (t >= T) return;
+  const u32x4_t *src = x + (size_t)t * nvec;
+  for (int seg = 0; seg < nvec; seg += 64 * NV) {
+    u32x4_t r[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = seg + i * 64 + lane;
+      if (c < nvec) r[i] = __builtin_nontemporal_load(src + c);
+    }
+    for (int k = 0; k < K; ++k) {
+      const int dr = dest_rank[(size_t)t * K + k];
+      if (dr != ep_rank) continue;
+      u32x4_t *dst = buf + (size_t)dest_row[(size_t)t * K + k] * nvec;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c = seg + i * 64 + lane;
+        if (c < nvec) dst[c] = r[i];
+      }
+    }
+  }
+}
+
+// Combine. Element type: bf16 (8 per vector) or fp32 (4 per vector).
+template <bool BF16, int NV>
+__global__ __launch_bounds__(256) void k_combine(
+    const u32x4_t *__restrict__ y, const int32_t *__restrict__ dest_rank,
+    const int32_t *__restrict__ dest_row, const float *__restrict__ w,
+    u32x4_t *__restrict__ out, int T, int K, int nvec, int ep_rank) {
+  constexpr int EPV = BF16 ? 8 : 4;  // elements per 16-byte vector
+  const int lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6));
+  if (t >= T) return;
+  for (int seg = 0; seg < nvec; seg += 64 * NV) {
+    float acc[NV][EPV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[i][e] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const size_t q = (size_t)t * K + k;
+      if (dest_rank[q] != ep_rank) continue;
+      const float wk = w[q];
+      const u32x4_t *src = y + (size_t)dest_row[q] * nvec;
+      u32x4_t v[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c = seg + i * 64 + lane;
+        if (c < nvec) v[i] = src[c];
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const uint32_t u[4] = {v[i][0], v[i][1], v[i][2], v[i][3]};
+        if constexpr (BF16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[i][2 * e] = fmaf(wk, bf16_lo(u[e]), acc[i][2 * e]);
+            acc[i][2 * e + 1] = fmaf(wk, bf16_hi(u[e]), acc[i][2 * e + 1]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wk, __uint_as_float(u[e]), acc[i][e]);
+        }
+      }
+    }
+    u32x4_t *dst = out + (size_t)t * nvec;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = seg + i * 64 + lane;
+      if (c >= nvec) continue;
+      u32x4_t o;
+      if constexpr (BF16) {
+        o[0] = pack_bf16x2(acc[i][0], acc[i][1]);
+        o[1] = pack_bf16x2(acc[i][2], acc[i][3]);
+        o[2] = pack_bf16x2(acc[i][4], acc[i][5]);
+        o[3] = pack_bf16x2(acc[i][6], acc[i][7]);
+      } else {
+        o[0] = __float_as_uint(acc[i][0]);
+        o[1] = __float_as_uint(acc[i][1]);
+        o[2] = __float_as_uint(acc[i][2]);
+        o[3] = __float_as_uint(acc[i][3]);
+      }
+      __builtin_nontemporal_store(o, dst + c);
+    }
+  }
+}
+
+// Vectors-per-lane per pass: the smallest of 1,2,4,8 that covers the row.
+inline int pick_nv(int nvec) {
+  const int per_lane = (int)ceil_div(nvec, 64);
+  return per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : 8;
+}
+
+}  // namespace
+
+int launch_dispatch(const moe_shape_t &s, const void *x, const int32_t *dest_rank,
+                    const int32_t *dest_row, void *buf, hipStream_t st) {
+  const int nvec = s.d * elem_bytes(s.dtype) / 16;
+  const dim3 grid((unsigned)ceil_div(s.T, kRowsPerBlock)), block(256);
+  const u32x4_t *xv = static_cast<const u32x4_t *>(x);
+  u32x4_t *bv = static_cast<u32x4_t *>(buf);
+  switch (pick_nv(nvec)) {
+    case 1: hipLaunchKernelGGL(k_dispatch<1>, grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank); break;
+    case 2: hipLaunchKernelGGL(k_dispatch<2>, grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank); break;
+    case 4: hipLaunchKernelGGL(k_dispatch<4>, grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank); break;
+    default: hipLaunchKernelGGL(k_dispatch<8>, grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank); break;
+  }
+  return launch_status();
+}
+
+template <bool BF16>
+static void combine_nv(int nv, dim3 grid, hipStream_t st, const u32x4_t *y, const int32_t *dr,
+                       const int32_t *drow, const float *w, u32x4_t *o, const moe_shape_t &s,
+                       int nvec) {
+  switch (nv) {
+    case 1: hipLaunchKernelGGL((k_combine<BF16, 1>), grid, dim3(256), 0, st, y, dr, drow, w, o, s.T, s.K, nvec, s.ep_rank); break;
+    case 2: hipLaunchKernelGGL((k_combine<BF16, 2>), grid, dim3(256), 0, st, y, dr, drow, w, o, s.T, s.K, nvec, s.ep_rank); break;
+    case 4: hipLaunchKernelGGL((k_combine<BF16, 4>), grid, dim3(256), 0, st, y, dr, drow, w, o, s.T, s.K, nvec, s.ep_rank); break;
+    default: hipLaunchKernelGGL((k_combine<BF16, 8>), grid, dim3(256), 0, st, y, dr, drow, w, o, s.T, s.K, nvec, s.ep_rank); break;
+  }
+}
+
+int launch_combine(const moe_shape_t &s, const void *y, const int32_t *dest_rank,
+                   const int32_t *dest_row, const float *w, void *out, hipStream_t st) {
+  const int nvec = s.d * elem_bytes(s.dtype) / 16;
+  const dim3 grid((unsigned)ceil_div(s.T, kRowsPerBlock));
+  const u32x4_t *yv = static_cast<const u32x4_t *>(y);
+  u32x4_t *ov = static_cast<u32x4_t *>(out);
+  if (s.dtype == MOE_BF16)
+    combine_nv<true>(pick_nv(nvec), grid, st, yv, dest_rank, dest_row, w, ov, s, nvec);
+  else
+    combine_nv<false>(pick_nv(nvec), grid, st, yv, dest_rank, dest_row, w, ov, s, nvec);
+  return launch_status();
+}
+
+}  // namespace moe

@@ -1,0 +1,179 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed-expert MoE forward layer.
+ *
+ * The layer runs in four stream-ordered calls, the rowwise path of the
+ * Olmo-core MoE report (Sec. 05 "Expert Parallelism", Sec. 5.4 and Fig. 16):
+ *
+ *   moe_route          top-K gating + route metadata (counts, offsets, route map)
+ *   moe_dispatch_rows  each kept route's token row copied into its capacity row
+ *   moe_expert_ffn     grouped SwiGLU expert FFN over each expert's valid rows
+ *   moe_combine        router-weighted gather back to token order
+ *
+ * General conventions (apply to every call):
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *     the moe_shape_t / moe_route_out_t structs themselves and the size_t
+ *     out-parameter of moe_route_workspace_size, which are host memory.
+ *   - Sizes are element counts; matrices are row-major and dense.
+ *   - Every call is enqueued on `stream` (0 = the null stream) and returns
+ *     without waiting. Outputs are valid once the stream reaches that point.
+ *     The library never copies device data to the host, never synchronizes,
+ *     never allocates and keeps no state between calls (Olmo-core MoE report,
+ *     Sec. 08 "Synchronization-Free Training", Sec. 8.5: route metadata stays
+ *     on the device; capacity-shaped buffers are fixed before the loop).
+ *   - Only host arguments are validated. Return value 0 = success, otherwise
+ *     one of the negative MOE_E* codes below; nothing is enqueued on error.
+ *   - Device-data preconditions that are NOT checked (checking would need a
+ *     device-to-host read): logits are finite; moe_route_map ids lie in
+ *     [-1, N) and the valid ids of one token are distinct; buf, h, y and out
+ *     do not alias each other or the inputs.
+ *   - Expert placement is contiguous: rank r owns global experts
+ *     [r*E_L, (r+1)*E_L), E_L = N / ep_size; this GPU is rank ep_rank and
+ *     holds only its E_L experts (AWS Neuron vLLM "Expert Parallelism (EP)"
+ *     design, weight layout across ranks).
+ *   - Capacity C is per expert; an expert keeps its first C routes in token
+ *     order and drops the rest. The caller computes C (normally
+ *     ceil(T*K*cf/N)) and sizes the buffers with it.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+/* Return codes. */
+#define MOE_OK          0
+#define MOE_EINVAL     -1  /* a size or index is out of range                      */
+#define MOE_EDTYPE     -2  /* unknown dtype                                         */
+#define MOE_EALIGN     -3  /* a data pointer is NULL or not 16-byte aligned         */
+#define MOE_EWORKSPACE -4  /* workspace NULL or smaller than moe_route_workspace_size */
+#define MOE_EHIP       -5  /* the HIP runtime rejected a kernel launch              */
+
+/* Limits of this implementation (MOE_EINVAL beyond them). */
+#define MOE_MAX_K        16     /* top-K                     */
+#define MOE_MAX_EXPERTS  1024   /* N                         */
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* Layer shape. T tokens, hidden d, N global experts, top-K, expert SwiGLU
+ * width F, ep_size expert shards of which this GPU is ep_rank, per-expert
+ * capacity C, and the dtype of x / buf / weights / h / y / out.
+ * Validated: all sizes >= 1, K <= N, K <= MOE_MAX_K, N <= MOE_MAX_EXPERTS,
+ * N % ep_size == 0, 0 <= ep_rank < ep_size, d and F multiples of 8,
+ * T*K < 2^31 and E_L*C < 2^31. */
+typedef struct {
+  int32_t T, d, N, K, F, ep_size, ep_rank, capacity;
+  moe_dtype_t dtype;
+} moe_shape_t;
+
+/* Outputs of moe_route / moe_route_map (all device pointers).
+ *   topk_idx  [T,K] int32  expert ids, logit-descending, ties -> lower id
+ *   topk_w    [T,K] fp32   softmax over the K selected logits
+ *   dest_rank [T,K] int32  owning rank of each kept route, -1 dropped/invalid
+ *   dest_row  [T,K] int32  row in that rank's capacity buffer, -1 dropped/invalid
+ *   drop_mask [T,K] uint8  1 = valid route dropped at capacity, else 0
+ *   counts    [N]   int32  routes per global expert before the capacity cut
+ *   offsets   [ep_size*(E_L+1)] int32  per rank r, entry r*(E_L+1)+j is the
+ *             number of kept rows of r's local experts j' < j (j = 0..E_L):
+ *             the cumulative offsets the grouped FFN consumes
+ *   row_src   [E_L*C] int32 or NULL   for rank ep_rank: t*K+k of the route
+ *             stored in each row, -1 on every row after the packed prefix
+ * Olmo-core MoE report Sec. 5.4: two [T,K] tensors give destination rank and
+ * destination row, negative entries mark invalid or capacity-dropped routes;
+ * the row is the expert's offset on its rank plus the number of earlier
+ * accepted routes for that expert. */
+typedef struct {
+  int32_t *topk_idx;
+  float   *topk_w;
+  int32_t *dest_rank;
+  int32_t *dest_row;
+  uint8_t *drop_mask;
+  int32_t *counts;
+  int32_t *offsets;
+  int32_t *row_src;
+} moe_route_out_t;
+
+/* Bytes of device workspace moe_route / moe_route_map need for `shape`.
+ * Returns MOE_EINVAL/MOE_EDTYPE for an invalid shape. */
+int moe_route_workspace_size(const moe_shape_t *shape, size_t *bytes);
+
+/* Top-K softmax gating and the route-map builder.
+ * logits [T,N] fp32 (device). For each token: the K largest logits (ties ->
+ * lower expert id, -0.0 == +0.0), their softmax weights (Olmo-core MoE report
+ * Sec. 05 Fig. 15: K ids and K weights per token, descending, summing to one),
+ * then counts, capacity admission in token order, offsets and the route map
+ * (Sec. 5.4, Fig. 16). All outputs except row_src are required; ws/ws_bytes
+ * is a device workspace of at least moe_route_workspace_size bytes (its
+ * contents on entry do not matter). */
+int moe_route(const moe_shape_t *shape, const float *logits, const moe_route_out_t *out,
+              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The route-map builder alone (Olmo-core MoE report Sec. 5.4): as moe_route
+ * but from given ids. topk_idx_in [T,K] int32, -1 = invalid route (gets
+ * dest_rank = dest_row = -1 and drop_mask = 0). out->topk_idx and
+ * out->topk_w are ignored and may be NULL. */
+int moe_route_map(const moe_shape_t *shape, const int32_t *topk_idx_in,
+                  const moe_route_out_t *out, void *ws, size_t ws_bytes,
+                  hipStream_t stream);
+
+/* Rowwise dispatch (Olmo-core MoE report Sec. 5.6, Table 8, dispatch forward:
+ * the token source pushes x_t to the capacity row of the selected expert;
+ * negative destinations are skipped). buf[dest_row[t,k]] = x[t] for every
+ * route with dest_rank[t,k] == ep_rank. x [T,d], buf [E_L*C, d] in dtype.
+ * Rows of buf after the packed prefix are neither read nor written. */
+int moe_dispatch_rows(const moe_shape_t *shape, const void *x, const int32_t *dest_rank,
+                      const int32_t *dest_row, void *buf, hipStream_t stream);
+
+/* Grouped expert SwiGLU FFN over the packed prefix (Olmo-core MoE report
+ * Sec. 5.7: experts packed back to back from row 0, grouped GEMM skips the
+ * tail; Sec. 08, Sec. 8.5: int32 device cumulative offsets, tail-aware
+ * SwiGLU). For each local expert j with rows [o_j, o_{j+1}) where
+ * o = offsets + ep_rank*(E_L+1):
+ *   G = X W_gu[j][0:F]^T,  U = X W_gu[j][F:2F]^T,  H = silu(G) * U,
+ *   Y = H W_d[j]^T
+ * buf [E_L*C, d], w_gu [E_L, 2F, d] (rows 0..F-1 gate, F..2F-1 up),
+ * w_down [E_L, d, F], h [E_L*C, F] (caller-owned scratch), y [E_L*C, d];
+ * all in dtype. Accumulation is fp32; H and Y are stored in dtype with
+ * round-to-nearest-even. Only prefix rows of h and y are written. */
+int moe_expert_ffn(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
+                   const void *w_gu, const void *w_down, void *h, void *y,
+                   hipStream_t stream);
+
+/* The two halves of moe_expert_ffn, same arguments and layouts:
+ * moe_expert_up writes h = silu(X W_gate^T) * (X W_up^T) for the prefix rows;
+ * moe_expert_down writes y = h W_d^T for the prefix rows. */
+int moe_expert_up(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
+                  const void *w_gu, void *h, hipStream_t stream);
+int moe_expert_down(const moe_shape_t *shape, const void *h, const int32_t *offsets,
+                    const void *w_down, void *y, hipStream_t stream);
+
+/* Weighted combine (Olmo-core MoE report Sec. 5.6, Table 8, combine forward:
+ * the token source pulls the selected expert rows and performs the
+ * router-weighted reduction; invalid entries gather zero). For every token t:
+ *   out[t] = sum over k ascending with dest_rank[t,k] == ep_rank of
+ *            topk_w[t,k] * y[dest_row[t,k]]
+ * accumulated in fp32 and stored in dtype; a token with no kept local route
+ * gets an exact zero row. On an expert shard this is the shard's partial
+ * output; the sum over all ranks is the full layer output (AWS Neuron EP
+ * design, "Why a single all-reduce works"). y [E_L*C, d], out [T,d]. */
+int moe_combine(const moe_shape_t *shape, const void *y, const int32_t *dest_rank,
+                const int32_t *dest_row, const float *topk_w, void *out,
+                hipStream_t stream);
+
+/* Human-readable text of a return code (static storage, never NULL). */
+const char *moe_strerror(int code);
+
+/* Validate a shape without enqueuing anything: MOE_OK or the error code the
+ * other calls would return for it. */
+int moe_validate_shape(const moe_shape_t *shape);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

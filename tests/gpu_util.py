@@ -1,0 +1,97 @@
+"""Helpers shared by the GPU parity tests: run the HIP layer stage by stage and
+compare with the CPU oracle. The oracle only ever receives inputs drawn by the
+seeded generators (or taken from the oracle itself); nothing computed by the
+HIP path is fed to it."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import combine_top_softmax_amd as moe
+from oracle import moe_oracle as orc
+
+BF16_NAN = -1   # int16 0xFFFF: a NaN in bfloat16
+F32_NAN = -1    # int32 0xFFFFFFFF: a NaN in fp32
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.to(torch.float64).numpy()
+    return t.numpy()
+
+
+def poison_(t: torch.Tensor) -> torch.Tensor:
+    """Fill with an all-ones bit pattern (NaN for bf16/fp32)."""
+    if t.dtype == torch.bfloat16:
+        t.view(torch.int16).fill_(BF16_NAN)
+    elif t.dtype == torch.float32:
+        t.view(torch.int32).fill_(F32_NAN)
+    else:
+        t.fill_(-1)
+    return t
+
+
+def is_poison(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16) == BF16_NAN
+    if t.dtype == torch.float32:
+        return t.view(torch.int32) == F32_NAN
+    return t == -1
+
+
+def tol_of(dtype: str) -> float:
+    return 2e-2 if dtype == "bf16" else 1e-4
+
+
+def assert_rows_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str) -> float:
+    """Per-row relative L2 error <= tol; rows that are exactly zero in the
+    reference must be exactly zero. Returns the worst per-row error."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    zero = np.all(ref == 0, axis=1)
+    assert np.all(got[zero] == 0), f"{what}: rows that must be exactly zero are not"
+    nz = ~zero
+    if not np.any(nz):
+        return 0.0
+    err = np.linalg.norm(got[nz] - ref[nz], axis=1) / np.linalg.norm(ref[nz], axis=1)
+    worst = float(err.max())
+    assert worst <= tol, f"{what}: worst per-row relative L2 error {worst:.3e} > {tol:.1e}"
+    return worst
+
+
+def route_gpu(shape: moe.MoeShape, logits_dev: torch.Tensor, row_src: bool = True):
+    out = moe.RouteOut.empty(shape, "cuda", row_src=row_src)
+    for t in (out.topk_idx, out.dest_rank, out.dest_row, out.counts, out.offsets):
+        t.fill_(-7)
+    if out.row_src is not None:
+        out.row_src.fill_(-7)
+    out.drop_mask.fill_(7)
+    out.topk_w.fill_(float("nan"))
+    ws = torch.empty(moe.moe_route_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)   # contents on entry must not matter
+    moe.moe_route(shape, logits_dev, out, ws)
+    return out
+
+
+def check_route(out: moe.RouteOut, ref: dict, shape: moe.MoeShape) -> None:
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(out.topk_idx), ref["topk_idx"])
+    np.testing.assert_allclose(to_np(out.topk_w), ref["topk_w"], rtol=1e-6, atol=0)
+    np.testing.assert_array_equal(to_np(out.counts), ref["counts"])
+    np.testing.assert_array_equal(to_np(out.offsets), ref["offsets"])
+    np.testing.assert_array_equal(to_np(out.dest_rank), ref["dest_rank"])
+    np.testing.assert_array_equal(to_np(out.dest_row), ref["dest_row"])
+    np.testing.assert_array_equal(to_np(out.drop_mask), ref["drop_mask"])
+    if out.row_src is not None:
+        np.testing.assert_array_equal(to_np(out.row_src), ref["row_src"])
+
+
+def oracle_route(cfg, logits_cpu: torch.Tensor) -> dict:
+    idx, w = orc.topk_softmax(logits_cpu.numpy(), cfg.K)
+    rm = orc.route_map(idx, cfg.N, cfg.ep_size, cfg.capacity, cfg.ep_rank)
+    rm["topk_idx"] = idx
+    rm["topk_w"] = w
+    return rm
