@@ -36,7 +36,32 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--traffic-probe", action="store_true",
+                   help="run 3 layer forwards, then 3 plain 512 MiB device copies (the "
+                        "calibration kernel for rocprofv3 FETCH_SIZE / WRITE_SIZE), and exit")
     return p.parse_args()
+
+
+def traffic_from_profile(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from profiles/<workload>_gemm_<kernel>_traffic.md,
+    or None when the file is missing or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_gemm_{kernel}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", "`")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        src = os.path.join(ROOT, kv["source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["source_sha256"]:
+            return None
+        return (float(kv["fetch_kib_per_launch"]) * float(kv["fetch_factor"]) +
+                float(kv["write_kib_per_launch"]) * float(kv["write_factor"])) * 1024.0
+    except (KeyError, ValueError, OSError):
+        return None
 
 
 def cpu_baseline(cfg, target_s: float) -> dict:
@@ -88,6 +113,17 @@ def main():
     inp = make_inputs(cfg, "cuda")
     layer = moe.MoELayer(shape, "cuda")
     stream = torch.cuda.current_stream()
+
+    if args.traffic_probe:
+        for _ in range(3):
+            layer.forward(inp.logits, inp.x, inp.w_gu, inp.w_d)
+        src = torch.empty(256 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("traffic probe done", flush=True)
+        return
 
     def step(ev=None):
         if ev: ev[0].record(stream)
@@ -151,7 +187,7 @@ def main():
         ach = flops[dominant] / (stage_ms[dominant] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": None, "kernel": dominant}
+                "traffic": traffic_from_profile(cfg.name, dominant), "kernel": dominant}
     elif dominant in flops:
         ach = flops[dominant] / (stage_ms[dominant] * 1e-3) / 1e12
         roof = {"bound": "alu", "achieved": round(ach, 3), "peak": FP32_VALU_PEAK_TFLOPS,

@@ -24,9 +24,13 @@
 // contiguous run of tiles (n-tiles of one m-tile, m-tiles of one expert),
 // which keeps the shared A rows and expert weights in that XCD's L2.
 //
-// bf16 path: 128 x 128 block tile, K step 64, 4 waves of 64 x 64, each a 2 x 2
-// grid of v_mfma_f32_32x32x16_bf16, LDS double buffer (rows padded by 16 bytes
-// so the 16-byte fragment reads of 16 lanes cover all 64 banks once).
+// bf16 paths (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
+//   k_gemm_bf16_big (K % 64 == 0): 256 x 256 block tile, 4 waves of 128 x 128
+//     (256 accumulators in AGPRs), operands loaded global -> LDS directly,
+//     XOR-swizzled LDS rows, two LDS stages, loads and fragment reads
+//     interleaved with the MFMAs (details at the kernel);
+//   k_gemm_bf16 (any K % 8 == 0): 128 x 128 block tile, 4 waves of 64 x 64,
+//     register-staged LDS double buffer with 16-byte row padding.
 // fp32 path: a plain LDS-tiled SIMT kernel (64 x 64 tile, 4 x 4 per thread).
 #include "moe_internal.h"
 
@@ -214,6 +218,250 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(
   }
 }
 
+// ------------------------------------------------------------ bf16 MFMA, big tiles
+// Block tile BM rows x 256 weight rows, K step BK, NS LDS stages, 4 waves
+// (the library instantiates BM = 256, BK = 64, NS = 2; the template also
+// covers BM = 128 and BK = 32, which measured slower):
+//   BM = 256: 2 x 2 waves of 128 x 128 (4 x 4 MFMA tiles, 256 accumulators)
+//   BM = 128: 1 x 4 waves of 128 x 64  (4 x 2 MFMA tiles)
+// Operands go global -> LDS directly (global_load_lds_dwordx4, no VGPR
+// staging). The loads of K step k + NS - 1 are issued right after the barrier
+// that opens step k, so each load has NS - 1 steps of MFMA work to land; the
+// barrier is a plain s_barrier preceded by a wait for this wave's loads of the
+// step about to be read (s_waitcnt vmcnt(N) with N = loads still allowed in
+// flight), not a full fence that would drain every outstanding load.
+// LDS rows are BK bf16 (BK/8 16-byte chunks); chunk c of row r is stored at
+// c ^ swz(r), chosen so that a wave's direct load writes whole rows
+// contiguously and the fragment reads of 16 consecutive rows (one chunk each)
+// touch 16 distinct 16-byte bank groups. Requires K % BK == 0.
+template <int BM, int BK, int NS>
+struct BigTile {
+  static constexpr int BW = 256;                 // weight rows per block
+  static constexpr int WAVES_M = BM / 128;
+  static constexpr int WAVES_N = 4 / WAVES_M;
+  static constexpr int WTN = BW / WAVES_N;       // weight rows per wave
+  static constexpr int TM = 4;                   // 32-row MFMA tiles per wave
+  static constexpr int TN = WTN / 32;            // 32-col MFMA tiles per wave
+  static constexpr int CH = BK / 8;              // 16-byte chunks per LDS row
+  static constexpr int ROW_B = BK * 2;           // bytes per LDS row
+  static constexpr int RPI = 64 / CH;            // rows per direct-load instruction
+  static constexpr int NA = BM / RPI / 4;        // A direct loads per wave per step
+  static constexpr int NB = BW / RPI / 4;        // B direct loads per wave per step
+  static constexpr int L = NA + NB;
+  static constexpr int KS = BK / 16;             // MFMA K sub-steps per step
+  static constexpr int A_BYTES = BM * ROW_B;
+  static constexpr int STAGE_BYTES = (BM + BW) * ROW_B;
+};
+
+template <int CH>
+__device__ __forceinline__ int chunk_swz(int r) {
+  if constexpr (CH == 8) return (r & 7) ^ ((r >> 3) & 1);
+  else return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
+}
+
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Issue the direct global -> LDS loads of one K step into `stage`.
+template <int BM, int BK, int NS>
+__device__ __forceinline__ void big_issue(const uint16_t *__restrict__ A,
+                                          const uint16_t *__restrict__ Wj, const uint32_t *a_off,
+                                          const uint32_t *b_off, int k0, int wv,
+                                          uint8_t *__restrict__ stage) {
+  using P = BigTile<BM, BK, NS>;
+#pragma unroll
+  for (int i = 0; i < P::NA; ++i)
+    __builtin_amdgcn_global_load_lds(A + a_off[i] + k0,
+                                     MOE_LDS(stage + (wv * P::NA + i) * 1024), 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < P::NB; ++i)
+    __builtin_amdgcn_global_load_lds(Wj + b_off[i] + k0,
+                                     MOE_LDS(stage + P::A_BYTES + (wv * P::NB + i) * 1024), 16,
+                                     0, 0);
+}
+
+// One main-loop step: run the MFMAs of this K step from `rd` while issuing
+// the direct loads of a later K step into `ld`. The stages are restrict
+// pointers so that, once inlined, the compiler does not wait for the loads
+// into `ld` before the reads of `rd`; the ordering the pipeline needs comes
+// from wait_vmcnt + s_barrier at the top of each step.
+//
+// Issue order inside a step is fixed with scheduling fences:
+//   * one direct load every (MFMAs per step / loads per step) MFMAs, so the
+//     address path is fed steadily instead of stalling issue at step start;
+//   * fragments double-buffered across the K sub-steps: each read of
+//     sub-step ks+1 follows one MFMA of sub-step ks, so it lands while the
+//     remaining MFMAs of ks execute.
+template <bool GATE_UP, int BM, int BK, int NS>
+__device__ __forceinline__ void big_step(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ Wj, const uint32_t *a_off,
+    const uint32_t *b_off, int k0, bool do_load, int wv, uint8_t *__restrict__ ld,
+    const uint8_t *__restrict__ rd, const int *fa, const int *fb, int khalf, int sw,
+    f32x16_t (&acc)[BigTile<BM, BK, NS>::TM][BigTile<BM, BK, NS>::TN]) {
+  using P = BigTile<BM, BK, NS>;
+  constexpr int MF = P::KS * P::TM * P::TN;      // MFMAs per step
+  // MFMAs between two direct loads: spread over the step, or over its first
+  // half with two stages (those loads must land before the next step)
+  constexpr int GAP = (NS == 2 && MF >= 2 * P::L) ? MF / (2 * P::L) : MF / P::L;
+  static_assert(GAP >= 1 && GAP * P::L <= MF, "load spacing");
+  auto issue_one = [&](int d) {
+    if (d < P::NA)
+      __builtin_amdgcn_global_load_lds(A + a_off[d] + k0,
+                                       MOE_LDS(ld + (wv * P::NA + d) * 1024), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(
+          Wj + b_off[d - P::NA] + k0,
+          MOE_LDS(ld + P::A_BYTES + (wv * P::NB + (d - P::NA)) * 1024), 16, 0, 0);
+  };
+  bf16x8_t fra[2][P::TM], frb[2][P::TN];
+  auto read_frag = [&](int buf, int ks, int q) {
+    const int cb = ((ks * 2 + khalf) ^ sw) << 4;
+    if (q < P::TM)
+      fra[buf][q] = *reinterpret_cast<const bf16x8_t *>(rd + fa[q] + cb);
+    else
+      frb[buf][q - P::TM] = *reinterpret_cast<const bf16x8_t *>(rd + fb[q - P::TM] + cb);
+  };
+#pragma unroll
+  for (int q = 0; q < P::TM + P::TN; ++q) read_frag(0, 0, q);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < P::KS; ++ks) {
+    const int cur = ks & 1;
+#pragma unroll
+    for (int q = 0; q < P::TM * P::TN; ++q) {
+      const int g = ks * P::TM * P::TN + q;
+      const int i = q / P::TN, j = q % P::TN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fra[cur][i], frb[cur][j], acc[i][j],
+                                                          0, 0, 0);
+      if (ks + 1 < P::KS && q < P::TM + P::TN) read_frag(cur ^ 1, ks + 1, q);
+      if (do_load && g % GAP == 0 && g / GAP < P::L) issue_one(g / GAP);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <bool GATE_UP, int BM, int BK, int NS>
+__global__ __launch_bounds__(256, 1) void k_gemm_bf16_big(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
+    const int32_t *__restrict__ off, uint16_t *__restrict__ Out, int E_L, int Kdim,
+    int Nout, int n_tiles_n) {
+  using P = BigTile<BM, BK, NS>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * P::STAGE_BYTES];
+
+  const Tile tl = find_tile(off, E_L, BM, n_tiles_n);
+  if (!tl.valid) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int wm = wv / P::WAVES_N, wn = wv % P::WAVES_N;
+  const int Nw = GATE_UP ? 2 * Nout : Nout;
+  const uint16_t *Wj = W + (size_t)tl.expert * Nw * Kdim;
+  const int n0 = tl.n_idx * (GATE_UP ? P::BW / 2 : P::BW);
+
+  // direct-load sources (element offsets): lane -> row RPI*instr + lane/CH,
+  // physical chunk lane%CH
+  uint32_t a_off[P::NA], b_off[P::NB];
+  {
+    const int lrow = lane / P::CH, pch = lane % P::CH;
+#pragma unroll
+    for (int i = 0; i < P::NA; ++i) {
+      const int r = (wv * P::NA + i) * P::RPI + lrow;
+      const int grow = min(tl.row0 + r, tl.row_end - 1);   // clamped rows are discarded
+      a_off[i] = (uint32_t)grow * (uint32_t)Kdim + ((pch ^ chunk_swz<P::CH>(r)) << 3);
+    }
+#pragma unroll
+    for (int i = 0; i < P::NB; ++i) {
+      const int r = (wv * P::NB + i) * P::RPI + lrow;
+      int wrow;
+      if (GATE_UP)
+        wrow = (r < P::BW / 2) ? min(n0 + r, Nout - 1) : Nout + min(n0 + r - P::BW / 2, Nout - 1);
+      else
+        wrow = min(n0 + r, Nout - 1);
+      b_off[i] = (uint32_t)wrow * (uint32_t)Kdim + ((pch ^ chunk_swz<P::CH>(r)) << 3);
+    }
+  }
+  // fragment read offsets (bytes within a stage)
+  const int fr = lane & 31;
+  const int sw = chunk_swz<P::CH>(fr);
+  const int khalf = lane >> 5;
+  int fa[P::TM], fb[P::TN];
+#pragma unroll
+  for (int t = 0; t < P::TM; ++t) fa[t] = (wm * 128 + t * 32 + fr) * P::ROW_B;
+#pragma unroll
+  for (int t = 0; t < P::TN; ++t) {
+    int brow;
+    if (GATE_UP)
+      brow = (t < P::TN / 2) ? wn * (P::WTN / 2) + t * 32
+                             : P::BW / 2 + wn * (P::WTN / 2) + (t - P::TN / 2) * 32;
+    else
+      brow = wn * P::WTN + t * 32;
+    fb[t] = P::A_BYTES + (brow + fr) * P::ROW_B;
+  }
+
+  f32x16_t acc[P::TM][P::TN];
+#pragma unroll
+  for (int i = 0; i < P::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < P::TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = Kdim / BK;
+  // prologue: K steps 0 .. NS-2 into stages 0 .. NS-2
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) big_issue<BM, BK, NS>(A, Wj, a_off, b_off, s * BK, wv, smem + s * P::STAGE_BYTES);
+  for (int kb = 0; kb < nk; ++kb) {
+    // this wave's loads of step kb have landed once at most the loads of
+    // steps kb+1 .. kb+NS-2 are still in flight; then every wave's have
+    if (kb + NS - 2 <= nk - 1) wait_vmcnt<(NS - 2) * P::L>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const int ls = (kb + NS - 1) % NS;   // stage read in step kb-1: free after the barrier
+    uint8_t *ld = smem + ls * P::STAGE_BYTES;
+    const uint8_t *rd = smem + (kb % NS) * P::STAGE_BYTES;
+    big_step<GATE_UP, BM, BK, NS>(A, Wj, a_off, b_off, (kb + NS - 1) * BK, kb + NS - 1 < nk, wv,
+                                  ld, rd, fa, fb, khalf, sw, acc);
+  }
+
+  // Epilogue (32x32 MFMA result: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
+  // column l%32 of the tile). Rows past the expert's last valid row are not written.
+#pragma unroll
+  for (int tm = 0; tm < P::TM; ++tm) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int grow = tl.row0 + wm * 128 + tm * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
+      if (grow < tl.row_end) {
+        uint16_t *orow = Out + (size_t)grow * Nout;
+        if (GATE_UP) {
+#pragma unroll
+          for (int tn = 0; tn < P::TN / 2; ++tn) {
+            const int col = n0 + wn * (P::WTN / 2) + tn * 32 + fr;
+            const float g = acc[tm][tn][r], u = acc[tm][tn + P::TN / 2][r];
+            if (col < Nout) orow[col] = f2bf(g / (1.0f + __expf(-g)) * u);
+          }
+        } else {
+#pragma unroll
+          for (int tn = 0; tn < P::TN; ++tn) {
+            const int col = n0 + wn * P::WTN + tn * 32 + fr;
+            if (col < Nout) orow[col] = f2bf(acc[tm][tn][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ fp32 SIMT
 constexpr int kFM = 64, kFW = 64, kFK = 16;
 
@@ -293,23 +541,41 @@ inline unsigned grid_blocks(const moe_shape_t &s, int bm, int n_tiles_n) {
   return (unsigned)(ceil_div(max_m * n_tiles_n, kNumXcd) * kNumXcd);
 }
 
+// Which bf16 kernel runs: the big-tile kernel (BM = 256, BK = 64, two
+// stages: the fastest of the tile / K-step / stage-count variants measured
+// on the named workloads) when K % 64 == 0, else the 128 x 128
+// register-staged kernel (any K % 8 == 0).
+template <bool GATE_UP>
+int launch_bf16(const moe_shape_t &s, const uint16_t *A, const uint16_t *W, const int32_t *off,
+                uint16_t *Out, int Kdim, int Nout, hipStream_t st) {
+  const int E_L = s.N / s.ep_size;
+  if (Kdim % 64 == 0) {
+    constexpr int BM = 256;
+    const int ntn = (int)ceil_div(Nout, GATE_UP ? 128 : 256);
+    hipLaunchKernelGGL((k_gemm_bf16_big<GATE_UP, BM, 64, 2>), dim3(grid_blocks(s, BM, ntn)),
+                       dim3(256), 0, st, A, W, off, Out, E_L, Kdim, Nout, ntn);
+  } else {
+    const int ntn = (int)ceil_div(Nout, GATE_UP ? kBW / 2 : kBW);
+    hipLaunchKernelGGL(k_gemm_bf16<GATE_UP>, dim3(grid_blocks(s, kBM, ntn)), dim3(256), 0, st,
+                       A, W, off, Out, E_L, Kdim, Nout, ntn);
+  }
+  return launch_status();
+}
+
 }  // namespace
 
 int launch_expert_up(const moe_shape_t &s, const void *buf, const int32_t *offsets,
                      const void *w_gu, void *h, hipStream_t st) {
   const int E_L = s.N / s.ep_size;
   const int32_t *off = offsets + (size_t)s.ep_rank * (E_L + 1);
-  if (s.dtype == MOE_BF16) {
-    const int ntn = (int)ceil_div(s.F, kBW / 2);
-    hipLaunchKernelGGL(k_gemm_bf16<true>, dim3(grid_blocks(s, kBM, ntn)), dim3(256), 0, st,
-                       static_cast<const uint16_t *>(buf), static_cast<const uint16_t *>(w_gu),
-                       off, static_cast<uint16_t *>(h), E_L, s.d, s.F, ntn);
-  } else {
-    const int ntn = (int)ceil_div(s.F, kFW / 2);
-    hipLaunchKernelGGL(k_gemm_f32<true>, dim3(grid_blocks(s, kFM, ntn)), dim3(256), 0, st,
-                       static_cast<const float *>(buf), static_cast<const float *>(w_gu), off,
-                       static_cast<float *>(h), E_L, s.d, s.F, ntn);
-  }
+  if (s.dtype == MOE_BF16)
+    return launch_bf16<true>(s, static_cast<const uint16_t *>(buf),
+                             static_cast<const uint16_t *>(w_gu), off, static_cast<uint16_t *>(h),
+                             s.d, s.F, st);
+  const int ntn = (int)ceil_div(s.F, kFW / 2);
+  hipLaunchKernelGGL(k_gemm_f32<true>, dim3(grid_blocks(s, kFM, ntn)), dim3(256), 0, st,
+                     static_cast<const float *>(buf), static_cast<const float *>(w_gu), off,
+                     static_cast<float *>(h), E_L, s.d, s.F, ntn);
   return launch_status();
 }
 
@@ -317,17 +583,14 @@ int launch_expert_down(const moe_shape_t &s, const void *h, const int32_t *offse
                        const void *w_d, void *y, hipStream_t st) {
   const int E_L = s.N / s.ep_size;
   const int32_t *off = offsets + (size_t)s.ep_rank * (E_L + 1);
-  if (s.dtype == MOE_BF16) {
-    const int ntn = (int)ceil_div(s.d, kBW);
-    hipLaunchKernelGGL(k_gemm_bf16<false>, dim3(grid_blocks(s, kBM, ntn)), dim3(256), 0, st,
-                       static_cast<const uint16_t *>(h), static_cast<const uint16_t *>(w_d), off,
-                       static_cast<uint16_t *>(y), E_L, s.F, s.d, ntn);
-  } else {
-    const int ntn = (int)ceil_div(s.d, kFW);
-    hipLaunchKernelGGL(k_gemm_f32<false>, dim3(grid_blocks(s, kFM, ntn)), dim3(256), 0, st,
-                       static_cast<const float *>(h), static_cast<const float *>(w_d), off,
-                       static_cast<float *>(y), E_L, s.F, s.d, ntn);
-  }
+  if (s.dtype == MOE_BF16)
+    return launch_bf16<false>(s, static_cast<const uint16_t *>(h),
+                              static_cast<const uint16_t *>(w_d), off, static_cast<uint16_t *>(y),
+                              s.F, s.d, st);
+  const int ntn = (int)ceil_div(s.d, kFW);
+  hipLaunchKernelGGL(k_gemm_f32<false>, dim3(grid_blocks(s, kFM, ntn)), dim3(256), 0, st,
+                     static_cast<const float *>(h), static_cast<const float *>(w_d), off,
+                     static_cast<float *>(y), E_L, s.F, s.d, ntn);
   return launch_status();
 }
 
