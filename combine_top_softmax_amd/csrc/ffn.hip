@@ -21,8 +21,9 @@
 // block id to a real tile and exits if there is none. The block id -> tile map
 // is XCD-aware: blocks are dealt to the 8 XCDs round-robin, so block b gets
 // tile (b % 8) * q + b / 8 (q = ceil(tiles / 8)) and each XCD walks a
-// contiguous run of tiles (n-tiles of one m-tile, m-tiles of one expert),
-// which keeps the shared A rows and expert weights in that XCD's L2.
+// contiguous run of tiles (the m-tiles of one expert for one weight panel,
+// then the next panel), which keeps the shared A rows and expert weights in
+// that XCD's L2.
 //
 // bf16 paths (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
 //   k_gemm_bf16_big (K % 64 == 0): 256 x 256 block tile, 4 waves of 128 x 128
@@ -50,6 +51,11 @@ struct Tile {
 
 // Map this block to a (expert, m-tile, n-tile) from the local offsets.
 // Executed redundantly by every wave of the block; the result is wave-uniform.
+// Tiles are numbered expert by expert; inside an expert with M m-tiles and
+// n_tiles_n n-tiles, they go in groups of NG n-tiles: all M m-tiles of the
+// first NG n-tiles, then the next group, so the tiles that run at the same
+// time on one XCD share both their A rows and their weight panels in L2.
+template <int NG>
 __device__ __forceinline__ Tile find_tile(const int32_t *__restrict__ off, int E_L, int bm,
                                           int n_tiles_n) {
   const int lane = threadIdx.x & 63;
@@ -68,8 +74,7 @@ __device__ __forceinline__ Tile find_tile(const int32_t *__restrict__ off, int E
   const int slot = b / kNumXcd;
   const int L = (b % kNumXcd) * q + slot;
   if (slot >= q || L >= total) return tl;
-  const int m_idx = L / n_tiles_n;
-  tl.n_idx = L - m_idx * n_tiles_n;
+  const int m_glob = L / n_tiles_n;      // which expert: the one holding m-tile m_glob
   int run = 0;
   for (int c = 0; c < E_L; c += 64) {
     const int j = c + lane;
@@ -77,15 +82,20 @@ __device__ __forceinline__ Tile find_tile(const int32_t *__restrict__ off, int E
     const int mt = (n + bm - 1) / bm;
     const int incl = wave_incl_scan(mt);
     const int tot = __shfl(incl, 63, 64);
-    if (m_idx < run + tot) {
-      const uint64_t hit = __ballot(m_idx < run + incl);
+    if (m_glob < run + tot) {
+      const uint64_t hit = __ballot(m_glob < run + incl);
       const int first = __builtin_ctzll(hit);
-      const int excl = __shfl(incl - mt, first, 64);
+      const int mstart = run + __shfl(incl - mt, first, 64);   // first m-tile of the expert
+      const int M = __shfl(mt, first, 64);
       const int e = c + first;
-      const int o0 = off[e];
+      const int li = L - mstart * n_tiles_n;                   // tile index inside the expert
+      const int g = li / (M * NG);                             // n-group
+      const int w = min(NG, n_tiles_n - g * NG);               // n-tiles in this group
+      const int r = li - g * NG * M;
       tl.expert = e;
-      tl.row0 = o0 + (m_idx - run - excl) * bm;
+      tl.row0 = off[e] + (r / w) * bm;
       tl.row_end = off[e + 1];
+      tl.n_idx = g * NG + r % w;
       tl.valid = true;
       return tl;
     }
@@ -93,6 +103,13 @@ __device__ __forceinline__ Tile find_tile(const int32_t *__restrict__ off, int E
   }
   return tl;
 }
+
+// n-tiles per group in the tile order (1 = all m-tiles of one n-tile, then the
+// next n-tile): equal or best on every named workload among 1, 2, 4, 8 and
+// "all n-tiles of an m-tile first".
+#ifndef MOE_TILE_NGROUP
+#define MOE_TILE_NGROUP 1
+#endif
 
 // ------------------------------------------------------------------ bf16 MFMA
 constexpr int kBM = 128;        // rows per block tile
@@ -108,7 +125,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kLds];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBW * kLds];
 
-  const Tile tl = find_tile(off, E_L, kBM, n_tiles_n);
+  const Tile tl = find_tile<MOE_TILE_NGROUP>(off, E_L, kBM, n_tiles_n);
   if (!tl.valid) return;
 
   const int tid = threadIdx.x;
@@ -355,7 +372,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_big(
   using P = BigTile<BM, BK, NS>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * P::STAGE_BYTES];
 
-  const Tile tl = find_tile(off, E_L, BM, n_tiles_n);
+  const Tile tl = find_tile<MOE_TILE_NGROUP>(off, E_L, BM, n_tiles_n);
   if (!tl.valid) return;
 
   const int tid = threadIdx.x;
@@ -434,30 +451,67 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_big(
                                   ld, rd, fa, fb, khalf, sw, acc);
   }
 
-  // Epilogue (32x32 MFMA result: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
-  // column l%32 of the tile). Rows past the expert's last valid row are not written.
+  // Epilogue, staged through LDS so that global stores are whole 16-byte
+  // vectors along output rows (the MFMA result layout gives each lane one
+  // column: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
+  // of its 32x32 tile).
+  //  1. neighbouring lanes swap one value (DPP quad permute 1,0,3,2) so each
+  //     lane holds two adjacent columns of one row and writes them as one
+  //     bf16x2 dword into a row-major LDS tile;
+  //  2. every thread copies 16-byte chunks of the tile to global memory,
+  //     skipping rows past the expert's last valid row and columns past Nout.
+  // LDS rows are OUTC bf16; 16-byte chunk c of row r sits at c ^ (4 * q(r))
+  // with q(r) = bit0(r) | bit2(r) << 1, so the four rows one dword write
+  // instruction touches (R, R+1, R+4, R+5) land in four distinct 64-byte
+  // bank groups.
+  constexpr int OUTC = GATE_UP ? P::BW / 2 : P::BW;    // output columns per block
+  constexpr int ROWB = OUTC * 2;                       // bytes per staged row
+  static_assert(BM * ROWB <= NS * P::STAGE_BYTES, "epilogue tile fits the stages");
+  __syncthreads();   // every wave is done reading the last stage
+  auto stage_off = [](int row, int colb) {   // byte offset of (row, byte column)
+    const int q = (row & 1) | (((row >> 2) & 1) << 1);
+    return row * ROWB + ((((colb >> 4) ^ (q << 2))) << 4) + (colb & 15);
+  };
+  const bool odd = (lane & 1) != 0;
 #pragma unroll
   for (int tm = 0; tm < P::TM; ++tm) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int grow = tl.row0 + wm * 128 + tm * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
-      if (grow < tl.row_end) {
-        uint16_t *orow = Out + (size_t)grow * Nout;
+    for (int tn = 0; tn < (GATE_UP ? P::TN / 2 : P::TN); ++tn) {
+      const int colb0 = (GATE_UP ? wn * (P::WTN / 2) : wn * P::WTN) * 2 + tn * 64;  // tile col * 2
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float v0, v1;
         if (GATE_UP) {
-#pragma unroll
-          for (int tn = 0; tn < P::TN / 2; ++tn) {
-            const int col = n0 + wn * (P::WTN / 2) + tn * 32 + fr;
-            const float g = acc[tm][tn][r], u = acc[tm][tn + P::TN / 2][r];
-            if (col < Nout) orow[col] = f2bf(g / (1.0f + __expf(-g)) * u);
-          }
+          const float g0 = acc[tm][tn][r], u0 = acc[tm][tn + P::TN / 2][r];
+          const float g1 = acc[tm][tn][r + 1], u1 = acc[tm][tn + P::TN / 2][r + 1];
+          v0 = g0 * __builtin_amdgcn_rcpf(1.0f + __expf(-g0)) * u0;
+          v1 = g1 * __builtin_amdgcn_rcpf(1.0f + __expf(-g1)) * u1;
         } else {
-#pragma unroll
-          for (int tn = 0; tn < P::TN; ++tn) {
-            const int col = n0 + wn * P::WTN + tn * 32 + fr;
-            if (col < Nout) orow[col] = f2bf(acc[tm][tn][r]);
-          }
+          v0 = acc[tm][tn][r];
+          v1 = acc[tm][tn][r + 1];
         }
+        // even lane keeps row r and takes its partner's row-r value; odd
+        // lane keeps row r+1 and takes its partner's row-(r+1) value
+        const float send = odd ? v0 : v1;
+        const float recv = __int_as_float(
+            __builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
+        const int row = wm * 128 + tm * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3) + (odd ? 1 : 0);
+        const int colb = colb0 + (fr & ~1) * 2;
+        const uint32_t packed = odd ? pack_bf16x2(recv, v1) : pack_bf16x2(v0, recv);
+        *reinterpret_cast<uint32_t *>(smem + stage_off(row, colb)) = packed;
       }
+    }
+  }
+  __syncthreads();
+  constexpr int CPR = ROWB / 16;                        // 16-byte chunks per row
+  const int ncols = min(OUTC, Nout - n0);               // multiple of 8
+  const int nrows = min(BM, tl.row_end - tl.row0);
+#pragma unroll 4
+  for (int idx = tid; idx < BM * CPR; idx += 256) {
+    const int row = idx / CPR, ch = idx % CPR;
+    if (row < nrows && ch * 8 < ncols) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(smem + stage_off(row, ch * 16));
+      *reinterpret_cast<uint4 *>(Out + (size_t)(tl.row0 + row) * Nout + n0 + ch * 8) = v;
     }
   }
 }
@@ -471,7 +525,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(
     float *__restrict__ Out, int E_L, int Kdim, int Nout, int n_tiles_n) {
   __shared__ float sA[kFK][kFM + 1];
   __shared__ float sB[kFK][kFW + 1];
-  const Tile tl = find_tile(off, E_L, kFM, n_tiles_n);
+  const Tile tl = find_tile<MOE_TILE_NGROUP>(off, E_L, kFM, n_tiles_n);
   if (!tl.valid) return;
   const int tid = threadIdx.x;
   const int ty = tid >> 4, tx = tid & 15;
