@@ -26,8 +26,8 @@
 // that XCD's L2.
 //
 // bf16 paths (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
-//   k_gemm_bf16_big (K % 64 == 0): 256 x 256 block tile, 4 waves of 128 x 128
-//     (256 accumulators in AGPRs), operands loaded global -> LDS directly,
+//   k_gemm_bf16_big (K % 64 == 0): 256 x 256 block tile, 8 waves of 128 x 64
+//     (two per SIMD), operands loaded global -> LDS directly,
 //     XOR-swizzled LDS rows, two LDS stages, loads and fragment reads
 //     interleaved with the MFMAs (details at the kernel);
 //   k_gemm_bf16 (any K % 8 == 0): 128 x 128 block tile, 4 waves of 64 x 64,
@@ -107,6 +107,12 @@ __device__ __forceinline__ Tile find_tile(const int32_t *__restrict__ off, int E
 // n-tiles per group in the tile order (1 = all m-tiles of one n-tile, then the
 // next n-tile): equal or best on every named workload among 1, 2, 4, 8 and
 // "all n-tiles of an m-tile first".
+// Waves per big-tile block: 8 (two per SIMD, 128 x 64 wave tiles, 128
+// accumulators each) measured 1-7% faster than 4 (one per SIMD, 128 x 128
+// wave tiles): twice as many waves keep operand loads in flight.
+#ifndef MOE_GEMM_WAVES
+#define MOE_GEMM_WAVES 8
+#endif
 #ifndef MOE_TILE_NGROUP
 #define MOE_TILE_NGROUP 1
 #endif
@@ -236,11 +242,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(
 }
 
 // ------------------------------------------------------------ bf16 MFMA, big tiles
-// Block tile BM rows x 256 weight rows, K step BK, NS LDS stages, 4 waves
-// (the library instantiates BM = 256, BK = 64, NS = 2; the template also
-// covers BM = 128 and BK = 32, which measured slower):
-//   BM = 256: 2 x 2 waves of 128 x 128 (4 x 4 MFMA tiles, 256 accumulators)
-//   BM = 128: 1 x 4 waves of 128 x 64  (4 x 2 MFMA tiles)
+// Block tile BM rows x 256 weight rows, K step BK, NS LDS stages, NW waves
+// (the library instantiates BM = 256, BK = 64, NS = 2, NW = 8; the template
+// also covers BM = 128, BK = 32 and NW = 4, which measured slower):
+//   NW = 8, BM = 256: 2 x 4 waves of 128 x 64 (4 x 2 MFMA tiles, 128 accumulators)
+//   NW = 4, BM = 256: 2 x 2 waves of 128 x 128 (4 x 4 MFMA tiles, 256 accumulators)
 // Operands go global -> LDS directly (global_load_lds_dwordx4, no VGPR
 // staging). The loads of K step k + NS - 1 are issued right after the barrier
 // that opens step k, so each load has NS - 1 steps of MFMA work to land; the
@@ -251,19 +257,20 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(
 // c ^ swz(r), chosen so that a wave's direct load writes whole rows
 // contiguously and the fragment reads of 16 consecutive rows (one chunk each)
 // touch 16 distinct 16-byte bank groups. Requires K % BK == 0.
-template <int BM, int BK, int NS>
+template <int BM, int BK, int NS, int NW = 4>
 struct BigTile {
+  static constexpr int NWAVES = NW;              // waves per block
   static constexpr int BW = 256;                 // weight rows per block
   static constexpr int WAVES_M = BM / 128;
-  static constexpr int WAVES_N = 4 / WAVES_M;
+  static constexpr int WAVES_N = NW / WAVES_M;
   static constexpr int WTN = BW / WAVES_N;       // weight rows per wave
   static constexpr int TM = 4;                   // 32-row MFMA tiles per wave
   static constexpr int TN = WTN / 32;            // 32-col MFMA tiles per wave
   static constexpr int CH = BK / 8;              // 16-byte chunks per LDS row
   static constexpr int ROW_B = BK * 2;           // bytes per LDS row
   static constexpr int RPI = 64 / CH;            // rows per direct-load instruction
-  static constexpr int NA = BM / RPI / 4;        // A direct loads per wave per step
-  static constexpr int NB = BW / RPI / 4;        // B direct loads per wave per step
+  static constexpr int NA = BM / RPI / NW;       // A direct loads per wave per step
+  static constexpr int NB = BW / RPI / NW;       // B direct loads per wave per step
   static constexpr int L = NA + NB;
   static constexpr int KS = BK / 16;             // MFMA K sub-steps per step
   static constexpr int A_BYTES = BM * ROW_B;
@@ -287,12 +294,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Issue the direct global -> LDS loads of one K step into `stage`.
-template <int BM, int BK, int NS>
+template <int BM, int BK, int NS, int NW>
 __device__ __forceinline__ void big_issue(const uint16_t *__restrict__ A,
                                           const uint16_t *__restrict__ Wj, const uint32_t *a_off,
                                           const uint32_t *b_off, int k0, int wv,
                                           uint8_t *__restrict__ stage) {
-  using P = BigTile<BM, BK, NS>;
+  using P = BigTile<BM, BK, NS, NW>;
 #pragma unroll
   for (int i = 0; i < P::NA; ++i)
     __builtin_amdgcn_global_load_lds(A + a_off[i] + k0,
@@ -316,13 +323,13 @@ __device__ __forceinline__ void big_issue(const uint16_t *__restrict__ A,
 //   * fragments double-buffered across the K sub-steps: each read of
 //     sub-step ks+1 follows one MFMA of sub-step ks, so it lands while the
 //     remaining MFMAs of ks execute.
-template <bool GATE_UP, int BM, int BK, int NS>
+template <bool GATE_UP, int BM, int BK, int NS, int NW>
 __device__ __forceinline__ void big_step(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ Wj, const uint32_t *a_off,
     const uint32_t *b_off, int k0, bool do_load, int wv, uint8_t *__restrict__ ld,
     const uint8_t *__restrict__ rd, const int *fa, const int *fb, int khalf, int sw,
-    f32x16_t (&acc)[BigTile<BM, BK, NS>::TM][BigTile<BM, BK, NS>::TN]) {
-  using P = BigTile<BM, BK, NS>;
+    f32x16_t (&acc)[BigTile<BM, BK, NS, NW>::TM][BigTile<BM, BK, NS, NW>::TN]) {
+  using P = BigTile<BM, BK, NS, NW>;
   constexpr int MF = P::KS * P::TM * P::TN;      // MFMAs per step
   // MFMAs between two direct loads: spread over the step, or over its first
   // half with two stages (those loads must land before the next step)
@@ -364,12 +371,12 @@ __device__ __forceinline__ void big_step(
   }
 }
 
-template <bool GATE_UP, int BM, int BK, int NS>
-__global__ __launch_bounds__(256, 1) void k_gemm_bf16_big(
+template <bool GATE_UP, int BM, int BK, int NS, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
     const int32_t *__restrict__ off, uint16_t *__restrict__ Out, int E_L, int Kdim,
     int Nout, int n_tiles_n) {
-  using P = BigTile<BM, BK, NS>;
+  using P = BigTile<BM, BK, NS, NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * P::STAGE_BYTES];
 
   const Tile tl = find_tile<MOE_TILE_NGROUP>(off, E_L, BM, n_tiles_n);
@@ -435,7 +442,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_big(
   // prologue: K steps 0 .. NS-2 into stages 0 .. NS-2
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) big_issue<BM, BK, NS>(A, Wj, a_off, b_off, s * BK, wv, smem + s * P::STAGE_BYTES);
+    if (s < nk)
+      big_issue<BM, BK, NS, NW>(A, Wj, a_off, b_off, s * BK, wv, smem + s * P::STAGE_BYTES);
   for (int kb = 0; kb < nk; ++kb) {
     // this wave's loads of step kb have landed once at most the loads of
     // steps kb+1 .. kb+NS-2 are still in flight; then every wave's have
@@ -447,7 +455,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_big(
     const int ls = (kb + NS - 1) % NS;   // stage read in step kb-1: free after the barrier
     uint8_t *ld = smem + ls * P::STAGE_BYTES;
     const uint8_t *rd = smem + (kb % NS) * P::STAGE_BYTES;
-    big_step<GATE_UP, BM, BK, NS>(A, Wj, a_off, b_off, (kb + NS - 1) * BK, kb + NS - 1 < nk, wv,
+    big_step<GATE_UP, BM, BK, NS, NW>(A, Wj, a_off, b_off, (kb + NS - 1) * BK, kb + NS - 1 < nk, wv,
                                   ld, rd, fa, fb, khalf, sw, acc);
   }
 
@@ -507,7 +515,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_big(
   const int ncols = min(OUTC, Nout - n0);               // multiple of 8
   const int nrows = min(BM, tl.row_end - tl.row0);
 #pragma unroll 4
-  for (int idx = tid; idx < BM * CPR; idx += 256) {
+  for (int idx = tid; idx < BM * CPR; idx += 64 * NW) {
     const int row = idx / CPR, ch = idx % CPR;
     if (row < nrows && ch * 8 < ncols) {
       const uint4 v = *reinterpret_cast<const uint4 *>(smem + stage_off(row, ch * 16));
@@ -606,8 +614,9 @@ int launch_bf16(const moe_shape_t &s, const uint16_t *A, const uint16_t *W, cons
   if (Kdim % 64 == 0) {
     constexpr int BM = 256;
     const int ntn = (int)ceil_div(Nout, GATE_UP ? 128 : 256);
-    hipLaunchKernelGGL((k_gemm_bf16_big<GATE_UP, BM, 64, 2>), dim3(grid_blocks(s, BM, ntn)),
-                       dim3(256), 0, st, A, W, off, Out, E_L, Kdim, Nout, ntn);
+    hipLaunchKernelGGL((k_gemm_bf16_big<GATE_UP, BM, 64, 2, MOE_GEMM_WAVES>),
+                       dim3(grid_blocks(s, BM, ntn)), dim3(64 * MOE_GEMM_WAVES), 0, st, A, W, off,
+                       Out, E_L, Kdim, Nout, ntn);
   } else {
     const int ntn = (int)ceil_div(Nout, GATE_UP ? kBW / 2 : kBW);
     hipLaunchKernelGGL(k_gemm_bf16<GATE_UP>, dim3(grid_blocks(s, kBM, ntn)), dim3(256), 0, st,
