@@ -150,6 +150,21 @@ def main():
     torch.cuda.set_sync_debug_mode(0)
     torch.cuda.synchronize()
 
+    # the same step replayed from a captured HIP graph (capacity-shaped buffers
+    # make the layer capturable): device time without per-call submission
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / args.steps
+
     total_ms = evs[0][0].elapsed_time(evs[-1][5])
     ms_step = total_ms / args.steps
     stage_ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
@@ -222,6 +237,7 @@ def main():
         "gemm_TFLOPs": round(6.0 * R * d * F / ffn_t / 1e12, 1),
         "gemm_mfma_frac": round(6.0 * R * d * F / ffn_t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "host_enqueue_ms_per_step": round(t_host * 1e3 / args.steps, 4),
+        "graph_replay_ms_per_step": round(graph_ms, 5),
         "stages": stages,
         "roofline": roof,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_seconds),

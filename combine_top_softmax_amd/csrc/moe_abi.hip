@@ -16,7 +16,7 @@ bool aligned4(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_
 int check_shape(const moe_shape_t *s) {
   if (s == nullptr) return MOE_EINVAL;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_EDTYPE;
-  if (s->T < 1 || s->d < 1 || s->N < 1 || s->K < 1 || s->F < 1 || s->ep_size < 1 ||
+  if (s->T < 0 || s->d < 1 || s->N < 1 || s->K < 1 || s->F < 1 || s->ep_size < 1 ||
       s->capacity < 1)
     return MOE_EINVAL;
   if (s->K > s->N || s->K > MOE_MAX_K || s->N > MOE_MAX_EXPERTS) return MOE_EINVAL;
@@ -36,12 +36,14 @@ size_t route_ws_bytes(const moe_shape_t &s) {
 
 int check_route_out(const moe_shape_t &s, const moe_route_out_t *o, bool need_topk) {
   if (o == nullptr) return MOE_EINVAL;
-  if (need_topk && (!aligned4(o->topk_idx) || !aligned4(o->topk_w))) return MOE_EALIGN;
-  if (!aligned4(o->dest_rank) || !aligned4(o->dest_row) || o->drop_mask == nullptr ||
-      !aligned4(o->counts) || !aligned4(o->offsets))
-    return MOE_EALIGN;
+  // the [T,K] arrays are not touched when T == 0 (they may then be NULL)
+  if (s.T > 0) {
+    if (need_topk && (!aligned4(o->topk_idx) || !aligned4(o->topk_w))) return MOE_EALIGN;
+    if (!aligned4(o->dest_rank) || !aligned4(o->dest_row) || o->drop_mask == nullptr)
+      return MOE_EALIGN;
+  }
+  if (!aligned4(o->counts) || !aligned4(o->offsets)) return MOE_EALIGN;
   if (o->row_src != nullptr && !aligned4(o->row_src)) return MOE_EALIGN;
-  (void)s;
   return MOE_OK;
 }
 
@@ -75,7 +77,7 @@ int moe_route(const moe_shape_t *shape, const float *logits, const moe_route_out
               void *ws, size_t ws_bytes, hipStream_t stream) {
   int rc = check_shape(shape);
   if (rc != MOE_OK) return rc;
-  if (!aligned16(logits)) return MOE_EALIGN;
+  if (shape->T > 0 && !aligned16(logits)) return MOE_EALIGN;
   if ((rc = check_route_out(*shape, out, true)) != MOE_OK) return rc;
   if (!aligned4(ws) || ws_bytes < route_ws_bytes(*shape)) return MOE_EWORKSPACE;
   return moe::launch_route(*shape, logits, nullptr, *out, ws, stream);
@@ -85,7 +87,7 @@ int moe_route_map(const moe_shape_t *shape, const int32_t *topk_idx_in,
                   const moe_route_out_t *out, void *ws, size_t ws_bytes, hipStream_t stream) {
   int rc = check_shape(shape);
   if (rc != MOE_OK) return rc;
-  if (!aligned4(topk_idx_in)) return MOE_EALIGN;
+  if (shape->T > 0 && !aligned4(topk_idx_in)) return MOE_EALIGN;
   if ((rc = check_route_out(*shape, out, false)) != MOE_OK) return rc;
   if (!aligned4(ws) || ws_bytes < route_ws_bytes(*shape)) return MOE_EWORKSPACE;
   return moe::launch_route(*shape, nullptr, topk_idx_in, *out, ws, stream);
@@ -95,6 +97,7 @@ int moe_dispatch_rows(const moe_shape_t *shape, const void *x, const int32_t *de
                       const int32_t *dest_row, void *buf, hipStream_t stream) {
   const int rc = check_shape(shape);
   if (rc != MOE_OK) return rc;
+  if (shape->T == 0) return MOE_OK;   // no token, nothing to move
   if (!aligned16(x) || !aligned16(buf) || !aligned4(dest_rank) || !aligned4(dest_row))
     return MOE_EALIGN;
   return moe::launch_dispatch(*shape, x, dest_rank, dest_row, buf, stream);
@@ -133,6 +136,7 @@ int moe_combine(const moe_shape_t *shape, const void *y, const int32_t *dest_ran
                 const int32_t *dest_row, const float *topk_w, void *out, hipStream_t stream) {
   const int rc = check_shape(shape);
   if (rc != MOE_OK) return rc;
+  if (shape->T == 0) return MOE_OK;   // no token, no output row
   if (!aligned16(y) || !aligned16(out) || !aligned4(dest_rank) || !aligned4(dest_row) ||
       !aligned4(topk_w))
     return MOE_EALIGN;

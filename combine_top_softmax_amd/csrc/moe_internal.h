@@ -17,7 +17,10 @@ constexpr int kNumXcd = 8;         // MI355X: 8 accelerator complex dies, each w
 // ---- host-side helpers -----------------------------------------------------
 inline int elem_bytes(moe_dtype_t dt) { return dt == MOE_F32 ? 4 : 2; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-inline int route_tiles(const moe_shape_t &s) { return (int)ceil_div(s.T, kRouteTile); }
+// at least one tile, so an empty batch still writes counts, offsets and row_src
+inline int route_tiles(const moe_shape_t &s) {
+  return s.T > 0 ? (int)ceil_div(s.T, kRouteTile) : 1;
+}
 
 // Launchers (return MOE_OK or MOE_EHIP). Shapes are already validated.
 int launch_route(const moe_shape_t &s, const float *logits, const int32_t *ids_in,

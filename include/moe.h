@@ -63,9 +63,13 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 /* Layer shape. T tokens, hidden d, N global experts, top-K, expert SwiGLU
  * width F, ep_size expert shards of which this GPU is ep_rank, per-expert
  * capacity C, and the dtype of x / buf / weights / h / y / out.
- * Validated: all sizes >= 1, K <= N, K <= MOE_MAX_K, N <= MOE_MAX_EXPERTS,
- * N % ep_size == 0, 0 <= ep_rank < ep_size, d and F multiples of 8,
- * T*K < 2^31 and E_L*C < 2^31. */
+ * Validated: T >= 0 and every other size >= 1, K <= N, K <= MOE_MAX_K,
+ * N <= MOE_MAX_EXPERTS, N % ep_size == 0, 0 <= ep_rank < ep_size, d and F
+ * multiples of 8, T*K < 2^31 and E_L*C < 2^31.
+ * An empty batch (T == 0) is valid: moe_route / moe_route_map write zero
+ * counts and offsets and a row_src of -1 (their [T,K] pointers may be NULL),
+ * moe_expert_ffn finds no row, and moe_dispatch_rows / moe_combine return
+ * MOE_OK without touching memory. */
 typedef struct {
   int32_t T, d, N, K, F, ep_size, ep_rank, capacity;
   moe_dtype_t dtype;

@@ -41,7 +41,7 @@ BASE = dict(T=64, d=64, N=8, K=2, F=64, ep_size=2, ep_rank=1, capacity=16, dtype
 
 
 @pytest.mark.parametrize("bad,code", [
-    (dict(T=0), _abi.MOE_EINVAL), (dict(d=0), _abi.MOE_EINVAL), (dict(K=9), _abi.MOE_EINVAL),
+    (dict(T=-1), _abi.MOE_EINVAL), (dict(d=0), _abi.MOE_EINVAL), (dict(K=9), _abi.MOE_EINVAL),
     (dict(K=0), _abi.MOE_EINVAL), (dict(N=9), _abi.MOE_EINVAL), (dict(ep_rank=2), _abi.MOE_EINVAL),
     (dict(ep_rank=-1), _abi.MOE_EINVAL), (dict(capacity=0), _abi.MOE_EINVAL),
     (dict(d=60), _abi.MOE_EINVAL), (dict(F=12), _abi.MOE_EINVAL),
@@ -52,6 +52,15 @@ BASE = dict(T=64, d=64, N=8, K=2, F=64, ep_size=2, ep_rank=1, capacity=16, dtype
 def test_validation_rejects_bad_shapes(bad, code):
     s = moe.MoeShape(**{**BASE, **bad})
     assert moe.moe_validate_shape(s) == code
+
+
+def test_empty_batch_is_a_valid_shape():
+    assert moe.moe_validate_shape(moe.MoeShape(**{**BASE, "T": 0})) == 0
+    lib = _abi.load()
+    s = moe.MoeShape(**{**BASE, "T": 0}).c()
+    # with no token, dispatch and combine touch nothing: NULL pointers are fine
+    assert lib.moe_dispatch_rows(ctypes.byref(s), None, None, None, None, None) == 0
+    assert lib.moe_combine(ctypes.byref(s), None, None, None, None, None, None) == 0
 
 
 def test_bad_dtype_and_null_pointers_return_codes():

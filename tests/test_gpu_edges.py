@@ -1,0 +1,135 @@
+"""GPU edge cases: the empty batch, a batch whose routes are all invalid,
+the implementation's maximum sizes (N = 1024 experts, K = 16, 16 KiB rows),
+and the layer replayed from a captured HIP graph."""
+from fractions import Fraction
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+import torch
+
+import combine_top_softmax_amd as moe
+from combine_top_softmax_amd.workloads import LayerConfig, make_inputs, random_ids
+from oracle import moe_oracle as orc
+from gpu_util import assert_rows_close, check_route, is_poison, poison_, to_np, tol_of
+
+pytestmark = pytest.mark.gpu
+
+
+def test_empty_batch_writes_zero_metadata():
+    shape = moe.MoeShape(T=0, d=64, N=16, K=4, F=64, ep_size=2, ep_rank=1, capacity=5,
+                         dtype="bf16")
+    layer = moe.MoELayer(shape, "cuda")
+    for t in (layer.route.counts, layer.route.offsets, layer.route.row_src):
+        t.fill_(-7)
+    poison_(layer.y)
+    logits = torch.empty(0, 16, device="cuda")
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    w_gu = torch.zeros(8, 128, 64, dtype=torch.bfloat16, device="cuda")
+    w_d = torch.zeros(8, 64, 64, dtype=torch.bfloat16, device="cuda")
+    out = layer.forward(logits, x, w_gu, w_d)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+    assert to_np(layer.route.counts).tolist() == [0] * 16
+    assert np.all(to_np(layer.route.offsets) == 0)
+    assert np.all(to_np(layer.route.row_src) == -1)
+    assert bool(is_poison(layer.y).all())          # the FFN found no row
+
+
+def test_all_routes_invalid_gives_zero_output():
+    cfg = LayerConfig("all_invalid", T=200, d=128, N=8, K=2, F=64, cf=Fraction(1), dtype="bf16",
+                      seed=41)
+    shape = moe.MoeShape.from_config(cfg)
+    inp = make_inputs(cfg, "cuda")
+    layer = moe.MoELayer(shape, "cuda")
+    poison_(layer.buf), poison_(layer.h), poison_(layer.y), poison_(layer.out)
+    ids = torch.full((cfg.T, cfg.K), -1, dtype=torch.int32, device="cuda")
+    moe.moe_route_map(shape, ids, layer.route, layer.ws)
+    layer.route.topk_w.fill_(0.5)
+    layer.dispatch_step(inp.x)
+    layer.up_step(inp.w_gu)
+    layer.down_step(inp.w_d)
+    layer.combine_step()
+    torch.cuda.synchronize()
+    assert np.all(to_np(layer.route.dest_row) == -1) and np.all(to_np(layer.route.drop_mask) == 0)
+    assert np.all(to_np(layer.route.offsets) == 0)
+    assert bool(is_poison(layer.buf).all()) and bool(is_poison(layer.y).all())
+    assert torch.count_nonzero(layer.out).item() == 0
+
+
+def test_maximum_expert_count_and_top_k():
+    """N = MOE_MAX_EXPERTS, K = MOE_MAX_K: 16 ballot chunks, the widest top-K list."""
+    cfg = LayerConfig("max_nk", T=700, d=64, N=1024, K=16, F=64, cf=Fraction(2), dtype="bf16",
+                      ep_size=4, ep_rank=2, seed=42)
+    inp = make_inputs(cfg, "cpu")
+    shape = moe.MoeShape.from_config(cfg)
+    layer = moe.MoELayer(shape, "cuda")
+    out = layer.forward(inp.logits.cuda(), inp.x.cuda(), inp.w_gu.cuda(), inp.w_d.cuda())
+    torch.cuda.synchronize()
+    ref = orc.moe_layer(inp.logits.numpy(), inp.x.double().numpy(), inp.w_gu.double().numpy(),
+                        inp.w_d.double().numpy(), cfg.K, cfg.capacity, cfg.ep_size, cfg.ep_rank,
+                        cfg.dtype)
+    check_route(layer.route, ref, shape)
+    assert_rows_close(to_np(out), ref["out"], tol_of(cfg.dtype), "out")
+
+
+def test_route_map_maximum_sizes_with_invalid():
+    T, N, K, C, ep = 3000, 1024, 16, 60, 8
+    ids = random_ids(T, N, K, seed=43, invalid_frac=0.05)
+    shape = moe.MoeShape(T=T, d=8, N=N, K=K, F=8, ep_size=ep, ep_rank=5, capacity=C, dtype="f32")
+    out = moe.RouteOut.empty(shape, "cuda")
+    ws = torch.empty(moe.moe_route_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    moe.moe_route_map(shape, ids.cuda(), out, ws)
+    ref = orc.route_map(ids.numpy(), N, ep, C, 5)
+    torch.cuda.synchronize()
+    for k in ("counts", "offsets", "dest_rank", "dest_row", "drop_mask", "row_src"):
+        np.testing.assert_array_equal(to_np(getattr(out, k)), ref[k], err_msg=k)
+
+
+def test_wide_rows_span_several_row_passes():
+    """d = 8192 bf16 (16 KiB rows): dispatch and combine loop over row segments."""
+    cfg = LayerConfig("wide_rows", T=96, d=8192, N=8, K=2, F=64, cf=Fraction(1), dtype="bf16",
+                      seed=44)
+    inp = make_inputs(cfg, "cpu")
+    shape = moe.MoeShape.from_config(cfg)
+    layer = moe.MoELayer(shape, "cuda")
+    poison_(layer.buf)
+    out = layer.forward(inp.logits.cuda(), inp.x.cuda(), inp.w_gu.cuda(), inp.w_d.cuda())
+    torch.cuda.synchronize()
+    ref = orc.moe_layer(inp.logits.numpy(), inp.x.double().numpy(), inp.w_gu.double().numpy(),
+                        inp.w_d.double().numpy(), cfg.K, cfg.capacity, cfg.ep_size, cfg.ep_rank,
+                        cfg.dtype)
+    n = int(ref["offsets"][0, -1])
+    np.testing.assert_array_equal(to_np(layer.buf[:n]), ref["buf"][:n])
+    assert_rows_close(to_np(out), ref["out"], tol_of(cfg.dtype), "out")
+
+
+def test_layer_replays_from_a_captured_graph():
+    """Fixed capacity-shaped buffers make the layer capturable (the pages use
+    graph replay as a diagnostic ceiling for submission cost). Every replay,
+    with new inputs copied in between, must equal the eager forward bitwise."""
+    cfg = LayerConfig("graph", T=1000, d=256, N=16, K=4, F=192, cf=Fraction(5, 4), dtype="bf16",
+                      seed=45)
+    shape = moe.MoeShape.from_config(cfg)
+    inp = make_inputs(cfg, "cuda")
+    static = SimpleNamespace(logits=inp.logits.clone(), x=inp.x.clone())
+    layer = moe.MoELayer(shape, "cuda")
+    layer.forward(static.logits, static.x, inp.w_gu, inp.w_d)   # warm up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(static.logits, static.x, inp.w_gu, inp.w_d)
+    eager = moe.MoELayer(shape, "cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(46)
+    for rep in range(3):
+        new_logits = torch.randn(cfg.T, cfg.N, generator=gen, device="cuda")
+        new_x = torch.randn(cfg.T, cfg.d, generator=gen, device="cuda").to(torch.bfloat16)
+        static.logits.copy_(new_logits)
+        static.x.copy_(new_x)
+        g.replay()
+        torch.cuda.synchronize()
+        ref = eager.forward(new_logits, new_x, inp.w_gu, inp.w_d)
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(layer.route.dest_row, eager.route.dest_row)
