@@ -1,4 +1,4 @@
-"""CPU oracle for the routed-expert MoE forward layer.
+"""CPU oracle for the routed-expert MoE layer: forward and backward.
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call this module. The product
@@ -19,6 +19,9 @@ with rowwise dispatch, as the pages describe it:
   * AWS Neuron vLLM "Expert Parallelism (EP)" design: contiguous expert-to-rank
     placement, every rank sees all tokens, partial sums over ranks add up to
     the full combine (GPT-OSS-20B case study, "Why a single all-reduce works").
+  * Backward: Olmo-core MoE report Sec. 5.6 Table 8 (adjoint row movements
+    sharing the saved route map, router-weight gradient from the gathered
+    expert outputs) and Sec. 5.7 (weight-gradient GEMMs over the valid prefix).
 
 Arithmetic is float64; values are rounded once to the layer's storage type at
 the points where the layer stores them (routing weights -> fp32; expert hidden
@@ -48,7 +51,8 @@ import numpy as np
 __all__ = [
     "round_bf16", "round_to", "topk_softmax", "route_map", "dispatch_rows",
     "silu", "expert_ffn", "expert_ffn_rows", "combine", "combine_tokens",
-    "moe_layer", "local_offsets",
+    "moe_layer", "local_offsets", "combine_bwd", "expert_ffn_bwd_rows", "expert_ffn_bwd",
+    "dispatch_bwd", "route_bwd", "moe_layer_bwd",
 ]
 
 
@@ -77,7 +81,10 @@ def round_bf16(v) -> np.ndarray:
 
 
 def round_to(v, dtype: str) -> np.ndarray:
-    """Round float64 values to the storage type ("f32" or "bf16"); float64 result."""
+    """Round float64 values to the storage type ("f32", "bf16", or "f64" = no
+    rounding, used by the finite-difference checks); float64 result."""
+    if dtype == "f64":
+        return np.asarray(v, dtype=np.float64)
     if dtype == "f32":
         return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
     if dtype == "bf16":
@@ -326,4 +333,133 @@ def moe_layer(logits, x, w_gu, w_d, K: int, C: int, ep_size: int, ep_rank: int, 
     out = combine(Y, rm["dest_rank"], rm["dest_row"], w, ep_rank, dtype)
     res = dict(rm)
     res.update(topk_idx=idx, topk_w=w, buf=buf, h=H, y=Y, out=out)
+    return res
+
+
+# --------------------------------------------------------------------------
+# Backward: the adjoint of each forward step
+# --------------------------------------------------------------------------
+# Olmo-core MoE report, Sec. 5.6 Table 8: backward reverses each forward
+# movement with the same saved route map -- combine backward pushes each
+# router-weighted output gradient to its expert-output-gradient row, dispatch
+# backward pulls the route gradients and sums them into the token's gradient;
+# the router-weight gradient comes from the gathered expert outputs and the
+# token-output gradient of the same accepted routes. Sec. 5.7: the expert
+# weight-gradient GEMMs run over the valid prefix only. Storage points mirror
+# the forward: expert-side activations and row gradients are stored in the
+# layer dtype, weight gradients and routing-weight gradients are float.
+
+def combine_bwd(dout, y, dest_rank, dest_row, w, ep_rank: int, n_rows: int, dtype: str):
+    """dY[row] = w[t,k] * dOut[t] (stored in dtype) and dw[t,k] = <dOut[t], Y[row]>
+    for every kept route of rank ``ep_rank``; dw = 0 for every other route.
+    Returns (dY [n_rows, d] float64, NaN on rows no route writes; dw [T, K] float64)."""
+    dout = np.asarray(dout, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    T, K = dest_rank.shape
+    dy = np.full((n_rows, dout.shape[1]), np.nan)
+    dw = np.zeros((T, K))
+    for t in range(T):
+        for k in range(K):
+            if dest_rank[t, k] == ep_rank and dest_row[t, k] >= 0:
+                r = int(dest_row[t, k])
+                dy[r] = round_to(float(w[t, k]) * dout[t], dtype)
+                dw[t, k] = float(np.dot(dout[t], y[r]))
+    return dy, dw
+
+
+def expert_ffn_bwd_rows(X, w_gu_j, w_d_j, H, dY, dtype: str):
+    """Backward of the SwiGLU MLP of one expert on rows X (see expert_ffn_rows).
+
+    G and U are recomputed from X and stored in dtype, as the forward stores H;
+    with s = sigmoid(G): dH = dY W_d, dG = dH * U * s * (1 + G (1 - s)),
+    dU = dH * G * s, [dG, dU] stored in dtype, dX = [dG, dU] W_gu stored in
+    dtype, dW_d = dY^T H and dW_gu = [dG, dU]^T X (float).
+    Returns dict(gu, dgu, dx, dw_gu, dw_d)."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(w_gu_j, dtype=np.float64)
+    Wd = np.asarray(w_d_j, dtype=np.float64)
+    F = W.shape[0] // 2
+    gu = round_to(X @ W.T, dtype)
+    G, U = gu[:, :F], gu[:, F:]
+    dH = np.asarray(dY, dtype=np.float64) @ Wd
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-G))
+    dG = dH * U * s * (1.0 + G * (1.0 - s))
+    dU = dH * G * s
+    dgu = round_to(np.concatenate([dG, dU], axis=1), dtype)
+    dx = round_to(dgu @ W, dtype)
+    dw_d = np.asarray(dY, dtype=np.float64).T @ np.asarray(H, dtype=np.float64)
+    dw_gu = dgu.T @ X
+    return {"gu": gu, "dgu": dgu, "dx": dx, "dw_gu": dw_gu, "dw_d": dw_d}
+
+
+def expert_ffn_bwd(buf, offsets_local, w_gu, w_d, H, dY, dtype: str):
+    """Grouped backward over each local expert's rows [off[j], off[j+1]).
+    Row outputs are NaN after the packed prefix; an expert with no row gets
+    zero weight gradients."""
+    E_L = len(offsets_local) - 1
+    rows = buf.shape[0]
+    F = w_gu.shape[1] // 2
+    d = w_d.shape[1]
+    res = {"gu": np.full((rows, 2 * F), np.nan), "dgu": np.full((rows, 2 * F), np.nan),
+           "dx": np.full((rows, d), np.nan), "dw_gu": np.zeros((E_L, 2 * F, d)),
+           "dw_d": np.zeros((E_L, d, F))}
+    for j in range(E_L):
+        a, b = int(offsets_local[j]), int(offsets_local[j + 1])
+        if b > a:
+            r = expert_ffn_bwd_rows(buf[a:b], w_gu[j], w_d[j], H[a:b], dY[a:b], dtype)
+            for k in ("gu", "dgu", "dx"):
+                res[k][a:b] = r[k]
+            res["dw_gu"][j] = r["dw_gu"]
+            res["dw_d"][j] = r["dw_d"]
+    return res
+
+
+def dispatch_bwd(dX, dest_rank, dest_row, ep_rank: int, dtype: str):
+    """dx[t] = sum over k ascending of dX[dest_row[t,k]] for the kept routes of
+    rank ``ep_rank`` (accumulated in float64, stored in dtype; zero when the
+    token has none). Returns [T, d] float64."""
+    dX = np.asarray(dX, dtype=np.float64)
+    T, K = dest_rank.shape
+    dx = np.zeros((T, dX.shape[1]))
+    for t in range(T):
+        for k in range(K):
+            if dest_rank[t, k] == ep_rank and dest_row[t, k] >= 0:
+                dx[t] += dX[int(dest_row[t, k])]
+    return round_to(dx, dtype)
+
+
+def route_bwd(idx, w, dw, N: int):
+    """Gradient of the logits through the softmax over the K selected logits:
+    dl[t, idx[t,k]] = w[t,k] * (dw[t,k] - sum_j w[t,j] dw[t,j]); zero on the
+    experts a token did not select (the selection itself is piecewise
+    constant). Returns [T, N] float64."""
+    idx = np.asarray(idx)
+    w = np.asarray(w, dtype=np.float64)
+    dw = np.asarray(dw, dtype=np.float64)
+    T, K = idx.shape
+    dl = np.zeros((T, N))
+    for t in range(T):
+        inner = float(np.dot(w[t], dw[t]))
+        for k in range(K):
+            dl[t, idx[t, k]] = w[t, k] * (dw[t, k] - inner)
+    return dl
+
+
+def moe_layer_bwd(fwd: dict, dout, x, w_gu, w_d, K: int, C: int, ep_size: int, ep_rank: int,
+                  dtype: str):
+    """Backward of moe_layer for the output gradient ``dout``, from the dict
+    ``fwd`` that moe_layer returned. Returns a dict with every intermediate and
+    the gradients dx [T,d], dlogits [T,N], dw_gu, dw_d."""
+    T, d = np.asarray(dout).shape
+    N = fwd["counts"].shape[0]
+    E_L = N // ep_size
+    n_rows = E_L * C
+    dy, dw = combine_bwd(dout, fwd["y"], fwd["dest_rank"], fwd["dest_row"], fwd["topk_w"],
+                         ep_rank, n_rows, dtype)
+    ffn = expert_ffn_bwd(fwd["buf"], fwd["offsets"][ep_rank], w_gu, w_d, fwd["h"], dy, dtype)
+    dx = dispatch_bwd(ffn["dx"], fwd["dest_rank"], fwd["dest_row"], ep_rank, dtype)
+    dl = route_bwd(fwd["topk_idx"], fwd["topk_w"], dw, N)
+    res = dict(ffn)
+    res.update(dy=dy, dw=dw, dx_rows=ffn["dx"], dx=dx, dlogits=dl)
     return res
