@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--no-backward", action="store_true",
+                   help="skip the timing of the layer backward (reported beside the forward)")
     p.add_argument("--traffic-probe", action="store_true",
                    help="run 3 layer forwards, then 3 plain 512 MiB device copies (the "
                         "calibration kernel for rocprofv3 FETCH_SIZE / WRITE_SIZE), and exit")
@@ -94,6 +96,55 @@ def cpu_baseline(cfg, target_s: float) -> dict:
                       f"the {cfg.name} shape, same input recipe, capacity recomputed for {T_s} "
                       f"tokens: {rows} routed rows in {dt:.2f} s; NumPy float64, "
                       f"BLAS threads={threads}"}
+
+
+BWD_STAGES = ["combine_bwd", "expert_ffn_bwd", "dispatch_bwd", "route_bwd"]
+
+
+def time_backward(args, layer, inp, stream, torch) -> dict:
+    """Layer backward after the forward's buffers (same route map): four calls
+    per step, timed with events between them. Not part of ``value``."""
+    from combine_top_softmax_amd.workloads import random_rows
+    import combine_top_softmax_amd as moe
+    cfg = layer.shape
+    dout = random_rows(cfg.T, cfg.d, cfg.torch_dtype, seed=12345, device="cuda")
+    layer.forward(inp.logits, inp.x, inp.w_gu, inp.w_d)
+    layer.alloc_backward("cuda")
+    s, r = layer.shape, layer.route
+
+    def bstep(ev=None):
+        if ev: ev[0].record(stream)
+        moe.moe_combine_bwd(s, dout, layer.y, r.dest_rank, r.dest_row, r.topk_w, layer.dy,
+                            layer.dw)
+        if ev: ev[1].record(stream)
+        moe.moe_expert_ffn_bwd(s, layer.buf, r.offsets, inp.w_gu, inp.w_d, layer.h, layer.dy,
+                               layer.gu, layer.gu, layer.dx_rows, layer.dw_gu, layer.dw_down)
+        if ev: ev[2].record(stream)
+        moe.moe_dispatch_bwd(s, layer.dx_rows, r.dest_rank, r.dest_row, layer.dx)
+        if ev: ev[3].record(stream)
+        moe.moe_route_bwd(s, r.topk_idx, r.topk_w, layer.dw, layer.dlogits)
+        if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        bstep()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.set_sync_debug_mode("error")
+    for i in range(args.steps):
+        bstep(evs[i])
+    torch.cuda.set_sync_debug_mode(0)
+    torch.cuda.synchronize()
+    ms = evs[0][0].elapsed_time(evs[-1][4]) / args.steps
+    st = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+          for i, n in enumerate(BWD_STAGES)}
+    R = int(r.offsets[s.ep_rank, -1].item())
+    # dH, dX, dW_d, dW_gu: 12 R d F; plus the recomputed [G U]: 4 R d F
+    fl = 12.0 * R * s.d * s.F
+    t_ffn = st["expert_ffn_bwd"] * 1e-3
+    return {"ms_per_step": round(ms, 5),
+            "stages_ms": {n: round(v, 5) for n, v in st.items()},
+            "expert_ffn_bwd_TFLOPs": round(fl / t_ffn / 1e12, 1),
+            "expert_ffn_bwd_TFLOPs_incl_recompute": round(fl * 16 / 12 / t_ffn / 1e12, 1)}
 
 
 def main():
@@ -164,6 +215,8 @@ def main():
     g1.record(stream)
     torch.cuda.synchronize()
     graph_ms = g0.elapsed_time(g1) / args.steps
+
+    backward = None if args.no_backward else time_backward(args, layer, inp, stream, torch)
 
     total_ms = evs[0][0].elapsed_time(evs[-1][5])
     ms_step = total_ms / args.steps
@@ -238,6 +291,7 @@ def main():
         "gemm_mfma_frac": round(6.0 * R * d * F / ffn_t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "host_enqueue_ms_per_step": round(t_host * 1e3 / args.steps, 4),
         "graph_replay_ms_per_step": round(graph_ms, 5),
+        "backward": backward,
         "stages": stages,
         "roofline": roof,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_seconds),

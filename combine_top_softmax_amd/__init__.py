@@ -22,7 +22,8 @@ from ._abi import MoeError  # noqa: F401
 __all__ = [
     "MoeShape", "RouteOut", "MoELayer", "MoeError", "moe_route_workspace_size", "moe_route",
     "moe_route_map", "moe_dispatch_rows", "moe_expert_ffn", "moe_expert_up",
-    "moe_expert_down", "moe_combine", "moe_strerror", "moe_validate_shape",
+    "moe_expert_down", "moe_combine", "moe_combine_bwd", "moe_expert_ffn_bwd",
+    "moe_dispatch_bwd", "moe_route_bwd", "moe_strerror", "moe_validate_shape",
 ]
 
 
@@ -233,6 +234,65 @@ def moe_combine(shape: MoeShape, y, dest_rank, dest_row, topk_w, out, stream=Non
     _abi.check("moe_combine", rc)
 
 
+# ----------------------------------------------------------------- backward
+def moe_combine_bwd(shape: MoeShape, dout, y, dest_rank, dest_row, topk_w, dy, dw,
+                    stream=None) -> None:
+    dt = shape.torch_dtype
+    _need(dout, "dout", (shape.T, shape.d), dt)
+    _need(y, "y", (shape.rows, shape.d), dt)
+    _need(dest_rank, "dest_rank", (shape.T, shape.K), torch.int32)
+    _need(dest_row, "dest_row", (shape.T, shape.K), torch.int32)
+    _need(topk_w, "topk_w", (shape.T, shape.K), torch.float32)
+    _need(dy, "dy", (shape.rows, shape.d), dt)
+    _need(dw, "dw", (shape.T, shape.K), torch.float32)
+    rc = _abi.load().moe_combine_bwd(ctypes.byref(shape.c()), _ptr(dout), _ptr(y),
+                                     _ptr(dest_rank), _ptr(dest_row), _ptr(topk_w), _ptr(dy),
+                                     _ptr(dw), _stream(stream))
+    _abi.check("moe_combine_bwd", rc)
+
+
+def moe_expert_ffn_bwd(shape: MoeShape, buf, offsets, w_gu, w_down, h, dy, gu, dgu, dx_rows,
+                       dw_gu, dw_down, stream=None) -> None:
+    dt = shape.torch_dtype
+    _need(buf, "buf", (shape.rows, shape.d), dt)
+    _ffn_checks(shape, offsets)
+    _need(w_gu, "w_gu", (shape.E_L, 2 * shape.F, shape.d), dt)
+    _need(w_down, "w_down", (shape.E_L, shape.d, shape.F), dt)
+    _need(h, "h", (shape.rows, shape.F), dt)
+    _need(dy, "dy", (shape.rows, shape.d), dt)
+    _need(gu, "gu", (shape.rows, 2 * shape.F), dt)
+    _need(dgu, "dgu", (shape.rows, 2 * shape.F), dt)
+    _need(dx_rows, "dx_rows", (shape.rows, shape.d), dt)
+    _need(dw_gu, "dw_gu", (shape.E_L, 2 * shape.F, shape.d), torch.float32)
+    _need(dw_down, "dw_down", (shape.E_L, shape.d, shape.F), torch.float32)
+    rc = _abi.load().moe_expert_ffn_bwd(
+        ctypes.byref(shape.c()), _ptr(buf), _ptr(offsets), _ptr(w_gu), _ptr(w_down), _ptr(h),
+        _ptr(dy), _ptr(gu), _ptr(dgu), _ptr(dx_rows), _ptr(dw_gu), _ptr(dw_down),
+        _stream(stream))
+    _abi.check("moe_expert_ffn_bwd", rc)
+
+
+def moe_dispatch_bwd(shape: MoeShape, dx_rows, dest_rank, dest_row, dx, stream=None) -> None:
+    dt = shape.torch_dtype
+    _need(dx_rows, "dx_rows", (shape.rows, shape.d), dt)
+    _need(dest_rank, "dest_rank", (shape.T, shape.K), torch.int32)
+    _need(dest_row, "dest_row", (shape.T, shape.K), torch.int32)
+    _need(dx, "dx", (shape.T, shape.d), dt)
+    rc = _abi.load().moe_dispatch_bwd(ctypes.byref(shape.c()), _ptr(dx_rows), _ptr(dest_rank),
+                                      _ptr(dest_row), _ptr(dx), _stream(stream))
+    _abi.check("moe_dispatch_bwd", rc)
+
+
+def moe_route_bwd(shape: MoeShape, topk_idx, topk_w, dw, dlogits, stream=None) -> None:
+    _need(topk_idx, "topk_idx", (shape.T, shape.K), torch.int32)
+    _need(topk_w, "topk_w", (shape.T, shape.K), torch.float32)
+    _need(dw, "dw", (shape.T, shape.K), torch.float32)
+    _need(dlogits, "dlogits", (shape.T, shape.N), torch.float32)
+    rc = _abi.load().moe_route_bwd(ctypes.byref(shape.c()), _ptr(topk_idx), _ptr(topk_w),
+                                   _ptr(dw), _ptr(dlogits), _stream(stream))
+    _abi.check("moe_route_bwd", rc)
+
+
 # ----------------------------------------------------------------- layer
 class MoELayer:
     """Capacity-shaped buffers allocated once; ``forward`` enqueues the four
@@ -273,3 +333,32 @@ class MoELayer:
                        stream)
         self.combine_step(stream)
         return self.out
+
+    def alloc_backward(self, device="cuda") -> None:
+        """Backward buffers, allocated once: dY, [G U] (reused in place for
+        [dG dU]), dX rows, dx, the weight and logit gradients."""
+        s = self.shape
+        dt = s.torch_dtype
+        self.dy = torch.empty(s.rows, s.d, dtype=dt, device=device)
+        self.gu = torch.empty(s.rows, 2 * s.F, dtype=dt, device=device)
+        self.dx_rows = torch.empty(s.rows, s.d, dtype=dt, device=device)
+        self.dx = torch.empty(s.T, s.d, dtype=dt, device=device)
+        self.dw = torch.empty(s.T, s.K, dtype=torch.float32, device=device)
+        self.dw_gu = torch.empty(s.E_L, 2 * s.F, s.d, dtype=torch.float32, device=device)
+        self.dw_down = torch.empty(s.E_L, s.d, s.F, dtype=torch.float32, device=device)
+        self.dlogits = torch.empty(s.T, s.N, dtype=torch.float32, device=device)
+
+    def backward(self, dout, w_gu, w_d, stream=None):
+        """Gradients of the last forward for the output gradient ``dout``:
+        returns (dx, dlogits, dw_gu, dw_down), enqueued on the stream with no
+        host synchronization."""
+        if not hasattr(self, "dy"):
+            self.alloc_backward(self.out.device)
+        s, r = self.shape, self.route
+        moe_combine_bwd(s, dout, self.y, r.dest_rank, r.dest_row, r.topk_w, self.dy, self.dw,
+                        stream)
+        moe_expert_ffn_bwd(s, self.buf, r.offsets, w_gu, w_d, self.h, self.dy, self.gu, self.gu,
+                           self.dx_rows, self.dw_gu, self.dw_down, stream)
+        moe_dispatch_bwd(s, self.dx_rows, r.dest_rank, r.dest_row, self.dx, stream)
+        moe_route_bwd(s, r.topk_idx, r.topk_w, self.dw, self.dlogits, stream)
+        return self.dx, self.dlogits, self.dw_gu, self.dw_down

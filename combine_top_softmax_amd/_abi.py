@@ -44,6 +44,10 @@ SIGNATURES = {
     "moe_expert_up": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_expert_down": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_combine": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P]),
+    "moe_combine_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_bwd": (ctypes.c_int, [_SHAPE] + [_P] * 12),
+    "moe_dispatch_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
+    "moe_route_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_validate_shape": (ctypes.c_int, [_SHAPE]),
 }

@@ -1,0 +1,543 @@
+// Backward of the MoE layer.
+//
+// Olmo-core MoE report, Sec. 05 "Expert Parallelism", Sec. 5.6 Table 8: the
+// backward reverses each forward movement with the same saved route map --
+// combine backward pushes each router-weighted output gradient to the
+// expert-output-gradient row of its route, dispatch backward pulls the route
+// gradients and sums them into the token's gradient, and the router-weight
+// gradient uses the gathered expert outputs with the token-output gradient of
+// the same accepted routes. Sec. 5.7: the expert GEMMs of the backward run over
+// the valid prefix only (the unwritten tail is skipped).
+//
+// Kernels:
+//   k_combine_bwd  wave per token: reads dOut[t] once per row segment, writes
+//                  w * dOut[t] to the dY row of each kept local route and the
+//                  dot <dOut[t], Y[row]> as that route's weight gradient (0 for
+//                  every other route).
+//   k_route_bwd    wave per token: logit gradient through the softmax over the
+//                  K selected logits, zero on the experts not selected.
+//   k_gemm_bwd     (bf16, MFMA) / k_gemm_bwd_f32 (fp32, SIMT): one grouped
+//                  GEMM for the four products of the expert backward:
+//                    DH: dH = dY W_d per expert over its rows, fused with the
+//                        SwiGLU backward on the recomputed G, U -> [dG dU]
+//                    DX: dX = [dG dU] W_gu per expert over its rows
+//                    WG: dW = P^T Q per expert, contracted over the expert's
+//                        rows (dW_d = dY^T H, dW_gu = [dG dU]^T X), fp32 out;
+//                        an expert without rows gets zeros.
+//                  The weights are N-contiguous in these products and the
+//                  weight-gradient left operand is M-contiguous; the bf16
+//                  kernel transposes those tiles while writing them to LDS, so
+//                  every MFMA operand is read K-contiguous.
+// G, U are recomputed by the forward NT GEMM (no activation, 2F columns);
+// dispatch backward is the forward combine kernel with unit weights.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRowsPerBlock = 4;   // 4 waves = 4 token rows per 256-thread block
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ------------------------------------------------------------ combine backward
+template <bool BF16, int NV>
+__global__ __launch_bounds__(256) void k_combine_bwd(
+    const u32x4_t *__restrict__ dout, const u32x4_t *__restrict__ y,
+    const int32_t *__restrict__ dest_rank, const int32_t *__restrict__ dest_row,
+    const float *__restrict__ w, u32x4_t *__restrict__ dy, float *__restrict__ dw, int T, int K,
+    int nvec, int ep_rank) {
+  const int lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6));
+  if (t >= T) return;
+  float dw_mine = 0.f;   // lane k < K accumulates route k's weight gradient
+  for (int seg = 0; seg < nvec; seg += 64 * NV) {
+    u32x4_t g[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = seg + i * 64 + lane;
+      g[i] = (c < nvec) ? dout[(size_t)t * nvec + c] : u32x4_t{0, 0, 0, 0};
+    }
+    for (int k = 0; k < K; ++k) {
+      const size_t q = (size_t)t * K + k;
+      if (dest_rank[q] != ep_rank) continue;
+      const size_t row = (size_t)dest_row[q];
+      const float wk = w[q];
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c = seg + i * 64 + lane;
+        if (c >= nvec) continue;
+        const u32x4_t yv = y[row * nvec + c];
+        u32x4_t o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (BF16) {
+            const float g0 = bf16_lo(g[i][e]), g1 = bf16_hi(g[i][e]);
+            dot = fmaf(g0, bf16_lo(yv[e]), dot);
+            dot = fmaf(g1, bf16_hi(yv[e]), dot);
+            o[e] = pack_bf16x2(wk * g0, wk * g1);
+          } else {
+            const float g0 = __uint_as_float(g[i][e]);
+            dot = fmaf(g0, __uint_as_float(yv[e]), dot);
+            o[e] = __float_as_uint(wk * g0);
+          }
+        }
+        dy[row * nvec + c] = o;
+      }
+      dot = wave_sum(dot);
+      if (lane == k) dw_mine += dot;
+    }
+  }
+  if (lane < K) dw[(size_t)t * K + lane] = dw_mine;
+}
+
+// ------------------------------------------------------------ router backward
+// dl[t, idx[t,k]] = w[t,k] * (dw[t,k] - sum_j w[t,j] dw[t,j]); 0 elsewhere.
+__global__ __launch_bounds__(256) void k_route_bwd(const int32_t *__restrict__ idx,
+                                                   const float *__restrict__ w,
+                                                   const float *__restrict__ dw,
+                                                   float *__restrict__ dl, int T, int N, int K) {
+  const int lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6));
+  if (t >= T) return;
+  const size_t base = (size_t)t * K;
+  float inner = 0.f;
+  for (int k = 0; k < K; ++k) inner = fmaf(w[base + k], dw[base + k], inner);
+  for (int e = lane; e < N; e += 64) {
+    float v = 0.f;
+    for (int k = 0; k < K; ++k)
+      if (idx[base + k] == e) v = w[base + k] * (dw[base + k] - inner);
+    dl[(size_t)t * N + e] = v;
+  }
+}
+
+// ------------------------------------------------------------ grouped GEMMs
+enum { BW_DH = 0, BW_DX = 1, BW_WG = 2 };
+
+struct RowTile {
+  int expert, row0, row_end, n_idx;
+  bool valid;
+};
+
+// Row-grouped modes: the same block -> (expert, m-tile, n-tile) map as the
+// forward grouped GEMM (device offsets, capacity-bound grid, XCD-aware
+// order: block b takes tile (b % 8) * q + b / 8).
+__device__ __forceinline__ RowTile find_row_tile(const int32_t *__restrict__ off, int E_L, int tm,
+                                                 int n_tiles_n) {
+  const int lane = threadIdx.x & 63;
+  RowTile tl;
+  tl.valid = false;
+  int total_m = 0;
+  for (int c = 0; c < E_L; c += 64) {
+    const int j = c + lane;
+    const int n = (j < E_L) ? off[j + 1] - off[j] : 0;
+    const int incl = wave_incl_scan((n + tm - 1) / tm);
+    total_m += __shfl(incl, 63, 64);
+  }
+  const int total = total_m * n_tiles_n;
+  const int q = (total + kNumXcd - 1) / kNumXcd;
+  const int b = blockIdx.x;
+  const int slot = b / kNumXcd;
+  const int L = (b % kNumXcd) * q + slot;
+  if (slot >= q || L >= total) return tl;
+  const int m_glob = L / n_tiles_n;
+  tl.n_idx = L - m_glob * n_tiles_n;
+  int run = 0;
+  for (int c = 0; c < E_L; c += 64) {
+    const int j = c + lane;
+    const int n = (j < E_L) ? off[j + 1] - off[j] : 0;
+    const int mt = (n + tm - 1) / tm;
+    const int incl = wave_incl_scan(mt);
+    const int tot = __shfl(incl, 63, 64);
+    if (m_glob < run + tot) {
+      const uint64_t hit = __ballot(m_glob < run + incl);
+      const int first = __builtin_ctzll(hit);
+      const int excl = __shfl(incl - mt, first, 64);
+      const int e = c + first;
+      tl.expert = e;
+      tl.row0 = off[e] + (m_glob - run - excl) * tm;
+      tl.row_end = off[e + 1];
+      tl.valid = true;
+      return tl;
+    }
+    run += tot;
+  }
+  return tl;
+}
+
+// Problem of one block: expert, output tile origin, valid rows, contraction range.
+struct Work {
+  int expert, m0, m_end, n0, kbeg, kend;
+};
+
+// Arguments shared by both element types.
+//   A(m, k) = A[m*lda + k] (DH, DX: rows of the expert)   or
+//   A(m, k) = A[(kbeg+k)*lda + m] (WG: M-contiguous rows of the expert)
+//   B(k, n) = Bj[(kbeg+k)*ldb + n], Bj = B + expert * b_expert_stride
+//   DH: N = F, K = d;  DX: N = d, K = 2F;  WG: M x N per expert, K = its rows
+struct GemmArgs {
+  const void *A;
+  int lda;
+  const void *B;
+  int ldb;
+  int64_t b_expert_stride;
+  const int32_t *off;
+  int E_L, M, N, Kdim;
+  const void *gu;   // DH: recomputed [G U] rows, [rows, 2F]
+  int F;
+  void *Out;
+  int ldo;
+  int64_t out_expert_stride;   // WG
+  int n_tiles_n, m_tiles;
+};
+
+template <int MODE>
+__device__ __forceinline__ bool get_work(const GemmArgs &p, int tm, int tn, Work &w) {
+  if constexpr (MODE == BW_WG) {
+    const int b = blockIdx.x;
+    w.expert = b / (p.m_tiles * p.n_tiles_n);
+    w.m0 = ((b / p.n_tiles_n) % p.m_tiles) * tm;
+    w.n0 = (b % p.n_tiles_n) * tn;
+    w.m_end = p.M;
+    w.kbeg = p.off[w.expert];
+    w.kend = p.off[w.expert + 1];
+    return true;
+  } else {
+    const RowTile tl = find_row_tile(p.off, p.E_L, tm, p.n_tiles_n);
+    if (!tl.valid) return false;
+    w.expert = tl.expert;
+    w.m0 = tl.row0;
+    w.m_end = tl.row_end;
+    w.n0 = tl.n_idx * tn;
+    w.kbeg = 0;
+    w.kend = p.Kdim;
+    return true;
+  }
+}
+
+// One output element: SwiGLU backward (DH), a dX row element (DX) or a
+// weight-gradient element (WG). T is the element type of the row tensors.
+template <int MODE, typename T>
+__device__ __forceinline__ void store_elem(const GemmArgs &p, const Work &w, int row, int col,
+                                           float v) {
+  if constexpr (MODE == BW_DH) {
+    const T *gr = static_cast<const T *>(p.gu) + (size_t)row * 2 * p.F;
+    T *o = static_cast<T *>(p.Out) + (size_t)row * p.ldo;
+    float g, u;
+    if constexpr (sizeof(T) == 2) {
+      g = __uint_as_float((uint32_t)gr[col] << 16);
+      u = __uint_as_float((uint32_t)gr[p.F + col] << 16);
+    } else {
+      g = gr[col];
+      u = gr[p.F + col];
+    }
+    const float s = 1.0f / (1.0f + __expf(-g));
+    const float dg = v * u * s * (1.0f + g * (1.0f - s));
+    const float du = v * g * s;
+    if constexpr (sizeof(T) == 2) {
+      o[col] = f2bf(dg);
+      o[p.F + col] = f2bf(du);
+    } else {
+      o[col] = dg;
+      o[p.F + col] = du;
+    }
+  } else if constexpr (MODE == BW_DX) {
+    T *o = static_cast<T *>(p.Out) + (size_t)row * p.ldo;
+    if constexpr (sizeof(T) == 2) o[col] = f2bf(v);
+    else o[col] = v;
+  } else {
+    static_cast<float *>(p.Out)[w.expert * p.out_expert_stride + (int64_t)row * p.ldo + col] = v;
+  }
+}
+
+// ---- bf16: 128 x 128 tile, K step 32, 4 waves of 64 x 64 (2 x 2 MFMA 32x32x16)
+constexpr int kT = 128;
+constexpr int kK = 32;
+constexpr int kLd = kK + 8;   // LDS row: 40 bf16 = 80 bytes (16-byte aligned, skewed banks)
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void k_gemm_bwd(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kT * kLd];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kT * kLd];
+  constexpr bool A_MCONTIG = MODE == BW_WG;
+  Work wk;
+  if (!get_work<MODE>(p, kT, kT, wk)) return;
+  const uint16_t *A = static_cast<const uint16_t *>(p.A);
+  const uint16_t *Bj = static_cast<const uint16_t *>(p.B) +
+                       (MODE == BW_WG ? 0 : (int64_t)wk.expert * p.b_expert_stride);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+
+  u32x4_t ra[2], rb[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = tid + 256 * i;
+      if constexpr (!A_MCONTIG) {
+        const int m = v >> 2, kv = v & 3;
+        const int mg = min(wk.m0 + m, wk.m_end - 1);   // rows past the expert: discarded
+        const int k = k0 + kv * 8;
+        ra[i] = (k < wk.kend) ? *reinterpret_cast<const u32x4_t *>(A + (size_t)mg * p.lda + k)
+                              : u32x4_t{0, 0, 0, 0};
+      } else {
+        const int kk = v >> 4, mv = v & 15;
+        const int r = wk.kbeg + k0 + kk;
+        const int m = wk.m0 + mv * 8;
+        ra[i] = (r < wk.kend && m < p.M)
+                    ? *reinterpret_cast<const u32x4_t *>(A + (size_t)r * p.lda + m)
+                    : u32x4_t{0, 0, 0, 0};
+      }
+      const int kk = v >> 4, nv = v & 15;
+      const int kr = wk.kbeg + k0 + kk;
+      const int n = wk.n0 + nv * 8;
+      rb[i] = (kr < wk.kend && n < p.N)
+                  ? *reinterpret_cast<const u32x4_t *>(Bj + (size_t)kr * p.ldb + n)
+                  : u32x4_t{0, 0, 0, 0};
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = tid + 256 * i;
+      if constexpr (!A_MCONTIG) {
+        const int m = v >> 2, kv = v & 3;
+        *reinterpret_cast<u32x4_t *>(&sA[m * kLd + kv * 8]) = ra[i];
+      } else {
+        const int kk = v >> 4, mv = v & 15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sA[(mv * 8 + 2 * e) * kLd + kk] = (uint16_t)(ra[i][e] & 0xffff);
+          sA[(mv * 8 + 2 * e + 1) * kLd + kk] = (uint16_t)(ra[i][e] >> 16);
+        }
+      }
+      const int kk = v >> 4, nv = v & 15;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sB[(nv * 8 + 2 * e) * kLd + kk] = (uint16_t)(rb[i][e] & 0xffff);
+        sB[(nv * 8 + 2 * e + 1) * kLd + kk] = (uint16_t)(rb[i][e] >> 16);
+      }
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = (wk.kend - wk.kbeg + kK - 1) / kK;
+  const int fr = lane & 31, khalf = lane >> 5;
+  if (nk > 0) {
+    gload(0);
+    sstore();
+    __syncthreads();
+  }
+  for (int kb = 0; kb < nk; ++kb) {
+    if (kb + 1 < nk) gload((kb + 1) * kK);
+#pragma unroll
+    for (int ks = 0; ks < kK / 16; ++ks) {
+      bf16x8_t a[2], b[2];
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms)
+        a[ms] = *reinterpret_cast<const bf16x8_t *>(
+            &sA[(wm * 64 + ms * 32 + fr) * kLd + ks * 16 + khalf * 8]);
+#pragma unroll
+      for (int ns = 0; ns < 2; ++ns)
+        b[ns] = *reinterpret_cast<const bf16x8_t *>(
+            &sB[(wn * 64 + ns * 32 + fr) * kLd + ks * 16 + khalf * 8]);
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns)
+          acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ms], b[ns], acc[ms][ns], 0, 0, 0);
+    }
+    __syncthreads();
+    if (kb + 1 < nk) {
+      sstore();
+      __syncthreads();
+    }
+  }
+
+  // register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
+#pragma unroll
+  for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wk.m0 + wm * 64 + ms * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
+        const int col = wk.n0 + wn * 64 + ns * 32 + fr;
+        if (row < wk.m_end && col < p.N) store_elem<MODE, uint16_t>(p, wk, row, col, acc[ms][ns][r]);
+      }
+}
+
+// ---- fp32: 64 x 64 tile, K step 16, 4 x 4 outputs per thread
+constexpr int kFT = 64;
+constexpr int kFK = 16;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void k_gemm_bwd_f32(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) float sA[kFK][kFT + 4];
+  __shared__ __attribute__((aligned(16))) float sB[kFK][kFT + 4];
+  Work wk;
+  if (!get_work<MODE>(p, kFT, kFT, wk)) return;
+  const float *A = static_cast<const float *>(p.A);
+  const float *Bj = static_cast<const float *>(p.B) +
+                    (MODE == BW_WG ? 0 : (int64_t)wk.expert * p.b_expert_stride);
+  const int tid = threadIdx.x;
+  const int ty = tid >> 4, tx = tid & 15;
+  float acc[4][4] = {};
+  const int klen = wk.kend - wk.kbeg;
+  for (int k0 = 0; k0 < klen; k0 += kFK) {
+    if constexpr (MODE != BW_WG) {
+      const int m = tid >> 2, kq = (tid & 3) * 4;
+      const int mg = min(wk.m0 + m, wk.m_end - 1);
+      const int k = k0 + kq;
+      const f32x4_t v = (k < wk.kend) ? *reinterpret_cast<const f32x4_t *>(A + (size_t)mg * p.lda + k)
+                                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sA[kq + e][m] = v[e];
+    } else {
+      const int kk = tid >> 4, mq = (tid & 15) * 4;
+      const int r = wk.kbeg + k0 + kk;
+      const int m = wk.m0 + mq;
+      const f32x4_t v = (r < wk.kend && m < p.M)
+                            ? *reinterpret_cast<const f32x4_t *>(A + (size_t)r * p.lda + m)
+                            : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4_t *>(&sA[kk][mq]) = v;
+    }
+    {
+      const int kk = tid >> 4, nq = (tid & 15) * 4;
+      const int kr = wk.kbeg + k0 + kk;
+      const int n = wk.n0 + nq;
+      const f32x4_t v = (kr < wk.kend && n < p.N)
+                            ? *reinterpret_cast<const f32x4_t *>(Bj + (size_t)kr * p.ldb + n)
+                            : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4_t *>(&sB[kk][nq]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kFK; ++kk) {
+      const f32x4_t a = *reinterpret_cast<const f32x4_t *>(&sA[kk][ty * 4]);
+      const f32x4_t b = *reinterpret_cast<const f32x4_t *>(&sB[kk][tx * 4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wk.m0 + ty * 4 + i, col = wk.n0 + tx * 4 + j;
+      if (row < wk.m_end && col < p.N) store_elem<MODE, float>(p, wk, row, col, acc[i][j]);
+    }
+}
+
+template <int MODE>
+void launch_mode(bool bf16, dim3 grid, const GemmArgs &p, hipStream_t st) {
+  if (bf16) hipLaunchKernelGGL(k_gemm_bwd<MODE>, grid, dim3(256), 0, st, p);
+  else hipLaunchKernelGGL(k_gemm_bwd_f32<MODE>, grid, dim3(256), 0, st, p);
+}
+
+template <bool BF16>
+void combine_bwd_nv(int nv, dim3 grid, hipStream_t st, const u32x4_t *g, const u32x4_t *y,
+                    const int32_t *dr, const int32_t *drow, const float *w, u32x4_t *o,
+                    float *dw, const moe_shape_t &s, int nvec) {
+  switch (nv) {
+    case 1: hipLaunchKernelGGL((k_combine_bwd<BF16, 1>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
+    case 2: hipLaunchKernelGGL((k_combine_bwd<BF16, 2>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
+    case 4: hipLaunchKernelGGL((k_combine_bwd<BF16, 4>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
+    default: hipLaunchKernelGGL((k_combine_bwd<BF16, 8>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
+  }
+}
+
+}  // namespace
+
+int launch_combine_bwd(const moe_shape_t &s, const void *dout, const void *y,
+                       const int32_t *dest_rank, const int32_t *dest_row, const float *w, void *dy,
+                       float *dw, hipStream_t st) {
+  const int nvec = s.d * elem_bytes(s.dtype) / 16;
+  const int per_lane = (int)ceil_div(nvec, 64);
+  const int nv = per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : 8;
+  const dim3 grid((unsigned)ceil_div(s.T, kRowsPerBlock));
+  const u32x4_t *g = static_cast<const u32x4_t *>(dout);
+  const u32x4_t *yv = static_cast<const u32x4_t *>(y);
+  u32x4_t *o = static_cast<u32x4_t *>(dy);
+  if (s.dtype == MOE_BF16)
+    combine_bwd_nv<true>(nv, grid, st, g, yv, dest_rank, dest_row, w, o, dw, s, nvec);
+  else
+    combine_bwd_nv<false>(nv, grid, st, g, yv, dest_rank, dest_row, w, o, dw, s, nvec);
+  return launch_status();
+}
+
+int launch_route_bwd(const moe_shape_t &s, const int32_t *idx, const float *w, const float *dw,
+                     float *dlogits, hipStream_t st) {
+  hipLaunchKernelGGL(k_route_bwd, dim3((unsigned)ceil_div(s.T, kRowsPerBlock)), dim3(256), 0, st,
+                     idx, w, dw, dlogits, s.T, s.N, s.K);
+  return launch_status();
+}
+
+int launch_expert_ffn_bwd(const moe_shape_t &s, const void *buf, const int32_t *offsets,
+                          const void *w_gu, const void *w_down, const void *h, const void *dy,
+                          void *gu, void *dgu, void *dx_rows, float *dw_gu, float *dw_down,
+                          hipStream_t st) {
+  const int E_L = s.N / s.ep_size;
+  const int d = s.d, F = s.F;
+  const bool bf16 = s.dtype == MOE_BF16;
+  const int tile = bf16 ? kT : kFT;
+  const int32_t *off = offsets + (size_t)s.ep_rank * (E_L + 1);
+  // 1. [G U] = X W_gu^T over the prefix rows (forward NT GEMM, no activation)
+  int rc = launch_gemm_nt(s, buf, w_gu, off, gu, d, 2 * F, st);
+  if (rc != MOE_OK) return rc;
+  const int64_t max_m = ceil_div((int64_t)E_L * s.capacity, tile) + E_L;
+  auto row_grid = [&](int ntn) {
+    return dim3((unsigned)(ceil_div(max_m * ntn, kNumXcd) * kNumXcd));
+  };
+  GemmArgs p{};
+  p.off = off;
+  p.E_L = E_L;
+  p.F = F;
+  // 2. dH = dY W_d (K = d, N = F), SwiGLU backward in the epilogue -> [dG dU]
+  p.A = dy; p.lda = d; p.B = w_down; p.ldb = F; p.b_expert_stride = (int64_t)d * F;
+  p.M = 0; p.N = F; p.Kdim = d; p.gu = gu; p.Out = dgu; p.ldo = 2 * F;
+  p.n_tiles_n = (int)ceil_div(F, tile);
+  launch_mode<BW_DH>(bf16, row_grid(p.n_tiles_n), p, st);
+  if ((rc = launch_status()) != MOE_OK) return rc;
+  // 3. dX = [dG dU] W_gu (K = 2F, N = d)
+  p.A = dgu; p.lda = 2 * F; p.B = w_gu; p.ldb = d; p.b_expert_stride = (int64_t)2 * F * d;
+  p.N = d; p.Kdim = 2 * F; p.gu = nullptr; p.Out = dx_rows; p.ldo = d;
+  p.n_tiles_n = (int)ceil_div(d, tile);
+  launch_mode<BW_DX>(bf16, row_grid(p.n_tiles_n), p, st);
+  if ((rc = launch_status()) != MOE_OK) return rc;
+  // 4. dW_d[j] = dY^T H over the expert's rows (M = d, N = F), fp32
+  p.A = dy; p.lda = d; p.B = h; p.ldb = F; p.b_expert_stride = 0;
+  p.M = d; p.N = F; p.Kdim = 0; p.Out = dw_down; p.ldo = F; p.out_expert_stride = (int64_t)d * F;
+  p.m_tiles = (int)ceil_div(d, tile); p.n_tiles_n = (int)ceil_div(F, tile);
+  launch_mode<BW_WG>(bf16, dim3((unsigned)(E_L * p.m_tiles * p.n_tiles_n)), p, st);
+  if ((rc = launch_status()) != MOE_OK) return rc;
+  // 5. dW_gu[j] = [dG dU]^T X over the expert's rows (M = 2F, N = d), fp32
+  p.A = dgu; p.lda = 2 * F; p.B = buf; p.ldb = d;
+  p.M = 2 * F; p.N = d; p.Out = dw_gu; p.ldo = d; p.out_expert_stride = (int64_t)2 * F * d;
+  p.m_tiles = (int)ceil_div(2 * F, tile); p.n_tiles_n = (int)ceil_div(d, tile);
+  launch_mode<BW_WG>(bf16, dim3((unsigned)(E_L * p.m_tiles * p.n_tiles_n)), p, st);
+  return launch_status();
+}
+
+}  // namespace moe

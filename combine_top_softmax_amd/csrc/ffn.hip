@@ -642,6 +642,19 @@ int launch_expert_up(const moe_shape_t &s, const void *buf, const int32_t *offse
   return launch_status();
 }
 
+int launch_gemm_nt(const moe_shape_t &s, const void *A, const void *W, const int32_t *off,
+                   void *Out, int Kdim, int Nout, hipStream_t st) {
+  const int E_L = s.N / s.ep_size;
+  if (s.dtype == MOE_BF16)
+    return launch_bf16<false>(s, static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(W),
+                              off, static_cast<uint16_t *>(Out), Kdim, Nout, st);
+  const int ntn = (int)ceil_div(Nout, kFW);
+  hipLaunchKernelGGL(k_gemm_f32<false>, dim3(grid_blocks(s, kFM, ntn)), dim3(256), 0, st,
+                     static_cast<const float *>(A), static_cast<const float *>(W), off,
+                     static_cast<float *>(Out), E_L, Kdim, Nout, ntn);
+  return launch_status();
+}
+
 int launch_expert_down(const moe_shape_t &s, const void *h, const int32_t *offsets,
                        const void *w_d, void *y, hipStream_t st) {
   const int E_L = s.N / s.ep_size;

@@ -143,4 +143,51 @@ int moe_combine(const moe_shape_t *shape, const void *y, const int32_t *dest_ran
   return moe::launch_combine(*shape, y, dest_rank, dest_row, topk_w, out, stream);
 }
 
+int moe_combine_bwd(const moe_shape_t *shape, const void *dout, const void *y,
+                    const int32_t *dest_rank, const int32_t *dest_row, const float *topk_w,
+                    void *dy, float *dw, hipStream_t stream) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (shape->T == 0) return MOE_OK;
+  if (!aligned16(dout) || !aligned16(y) || !aligned16(dy) || !aligned4(dest_rank) ||
+      !aligned4(dest_row) || !aligned4(topk_w) || !aligned4(dw))
+    return MOE_EALIGN;
+  return moe::launch_combine_bwd(*shape, dout, y, dest_rank, dest_row, topk_w, dy, dw, stream);
+}
+
+int moe_expert_ffn_bwd(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
+                       const void *w_gu, const void *w_down, const void *h, const void *dy,
+                       void *gu, void *dgu, void *dx_rows, float *dw_gu, float *dw_down,
+                       hipStream_t stream) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!aligned16(buf) || !aligned16(w_gu) || !aligned16(w_down) || !aligned16(h) ||
+      !aligned16(dy) || !aligned16(gu) || !aligned16(dgu) || !aligned16(dx_rows) ||
+      !aligned16(dw_gu) || !aligned16(dw_down) || !aligned4(offsets))
+    return MOE_EALIGN;
+  return moe::launch_expert_ffn_bwd(*shape, buf, offsets, w_gu, w_down, h, dy, gu, dgu, dx_rows,
+                                    dw_gu, dw_down, stream);
+}
+
+int moe_dispatch_bwd(const moe_shape_t *shape, const void *dx_rows, const int32_t *dest_rank,
+                     const int32_t *dest_row, void *dx, hipStream_t stream) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (shape->T == 0) return MOE_OK;
+  if (!aligned16(dx_rows) || !aligned16(dx) || !aligned4(dest_rank) || !aligned4(dest_row))
+    return MOE_EALIGN;
+  // the combine kernel with unit weights
+  return moe::launch_combine(*shape, dx_rows, dest_rank, dest_row, nullptr, dx, stream);
+}
+
+int moe_route_bwd(const moe_shape_t *shape, const int32_t *topk_idx, const float *topk_w,
+                  const float *dw, float *dlogits, hipStream_t stream) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (shape->T == 0) return MOE_OK;
+  if (!aligned4(topk_idx) || !aligned4(topk_w) || !aligned4(dw) || !aligned4(dlogits))
+    return MOE_EALIGN;
+  return moe::launch_route_bwd(*shape, topk_idx, topk_w, dw, dlogits, stream);
+}
+
 }  // extern "C"

@@ -33,6 +33,20 @@ int launch_expert_up(const moe_shape_t &s, const void *buf, const int32_t *offse
                      const void *w_gu, void *h, hipStream_t st);
 int launch_expert_down(const moe_shape_t &s, const void *h, const int32_t *offsets,
                        const void *w_d, void *y, hipStream_t st);
+// Out[r, :] = A[r] W[j]^T over the rows [off[j], off[j+1]) of each local expert
+// j (off already offset to this rank), W[j] = [Nout, Kdim]; no activation.
+int launch_gemm_nt(const moe_shape_t &s, const void *A, const void *W, const int32_t *off,
+                   void *Out, int Kdim, int Nout, hipStream_t st);
+// Backward.
+int launch_combine_bwd(const moe_shape_t &s, const void *dout, const void *y,
+                       const int32_t *dest_rank, const int32_t *dest_row, const float *w, void *dy,
+                       float *dw, hipStream_t st);
+int launch_route_bwd(const moe_shape_t &s, const int32_t *idx, const float *w, const float *dw,
+                     float *dlogits, hipStream_t st);
+int launch_expert_ffn_bwd(const moe_shape_t &s, const void *buf, const int32_t *offsets,
+                          const void *w_gu, const void *w_down, const void *h, const void *dy,
+                          void *gu, void *dgu, void *dx_rows, float *dw_gu, float *dw_down,
+                          hipStream_t st);
 
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;

@@ -11,7 +11,9 @@
 // lanes side by side, so every wave access is a contiguous 1 KiB segment.
 // Dispatch loads the source row once into registers and stores it to each
 // local destination. Combine accumulates in fp32, k ascending, and writes each
-// output row exactly once (no atomics, deterministic).
+// output row exactly once (no atomics, deterministic). With no weights it is
+// the dispatch backward: the plain sum of a token's route rows (Sec. 5.6,
+// Table 8, dispatch backward).
 #include "moe_internal.h"
 
 namespace moe {
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(256) void k_combine(
     for (int k = 0; k < K; ++k) {
       const size_t q = (size_t)t * K + k;
       if (dest_rank[q] != ep_rank) continue;
-      const float wk = w[q];
+      const float wk = w != nullptr ? w[q] : 1.0f;   // NULL: unit weights
       const u32x4_t *src = y + (size_t)dest_row[q] * nvec;
       u32x4_t v[NV];
 #pragma unroll

@@ -1,5 +1,6 @@
 /*
- * moe.h -- C ABI of the MI355X (gfx950) routed-expert MoE forward layer.
+ * moe.h -- C ABI of the MI355X (gfx950) routed-expert MoE layer (forward and
+ * backward).
  *
  * The layer runs in four stream-ordered calls, the rowwise path of the
  * Olmo-core MoE report (Sec. 05 "Expert Parallelism", Sec. 5.4 and Fig. 16):
@@ -168,6 +169,67 @@ int moe_expert_down(const moe_shape_t *shape, const void *h, const int32_t *offs
 int moe_combine(const moe_shape_t *shape, const void *y, const int32_t *dest_rank,
                 const int32_t *dest_row, const float *topk_w, void *out,
                 hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Backward. The adjoint of the forward calls for an output gradient dout,
+ * reusing the forward's saved route map and buffers (Olmo-core MoE report
+ * Sec. 5.6, Table 8: combine backward, dispatch backward and the
+ * router-weight gradient run on the same destination rank/row indices as the
+ * forward; Sec. 5.7: the expert backward GEMMs cover the packed prefix only).
+ * Order: moe_combine_bwd, moe_expert_ffn_bwd, moe_dispatch_bwd, moe_route_bwd.
+ * On an expert shard each call yields the shard's contribution; dx and dlogits
+ * of the whole layer are the sums over the ranks.
+ * ------------------------------------------------------------------------ */
+
+/* Combine backward (Table 8: the weighted output gradient is pushed to each
+ * accepted route's expert-output row; the router-weight gradient uses the
+ * gathered expert output with the same token's output gradient).
+ * dout [T,d] and y [E_L*C,d] (the forward's expert outputs) in dtype,
+ * topk_w [T,K] fp32. For every route with dest_rank[t,k] == ep_rank:
+ *   dy[dest_row[t,k]] = topk_w[t,k] * dout[t]      (stored in dtype)
+ *   dw[t,k]           = <dout[t], y[dest_row[t,k]]> (fp32 accumulation)
+ * every other route gets dw[t,k] = 0. dy [E_L*C,d]: exactly the packed prefix
+ * rows are written; dw [T,K] fp32 is fully written. T == 0: MOE_OK, nothing
+ * touched. */
+int moe_combine_bwd(const moe_shape_t *shape, const void *dout, const void *y,
+                    const int32_t *dest_rank, const int32_t *dest_row, const float *topk_w,
+                    void *dy, float *dw, hipStream_t stream);
+
+/* Expert FFN backward over each local expert j's rows [o_j, o_{j+1})
+ * (o = offsets + ep_rank*(E_L+1), as in moe_expert_ffn), with X = buf rows,
+ * H = h rows (the forward's) and dY = dy rows (from moe_combine_bwd):
+ *   [G U] = X W_gu[j]^T                          recomputed, stored in gu
+ *   dH = dY W_d[j],  s = sigmoid(G)
+ *   dG = dH * U * s * (1 + G*(1 - s)),  dU = dH * G * s   stored in dgu = [dG dU]
+ *   dx_rows = [dG dU] W_gu[j]
+ *   dw_down[j] = dY^T H,  dw_gu[j] = [dG dU]^T X     (fp32)
+ * gu, dgu [E_L*C, 2F] and dx_rows [E_L*C, d] in dtype: caller-owned, only the
+ * prefix rows are written; dgu may be the same buffer as gu (gu is then
+ * overwritten). Accumulation is fp32; row results are stored in dtype with
+ * round-to-nearest-even. dw_gu [E_L,2F,d] and dw_down [E_L,d,F] fp32 are fully
+ * overwritten (not accumulated into); an expert with no row gets zeros. */
+int moe_expert_ffn_bwd(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
+                       const void *w_gu, const void *w_down, const void *h, const void *dy,
+                       void *gu, void *dgu, void *dx_rows, float *dw_gu, float *dw_down,
+                       hipStream_t stream);
+
+/* Dispatch backward (Table 8: each token pulls its route gradients and sums
+ * them): dx[t] = sum over k ascending with dest_rank[t,k] == ep_rank of
+ * dx_rows[dest_row[t,k]], accumulated in fp32 and stored in dtype; a token
+ * with no kept local route gets an exact zero row. dx_rows [E_L*C,d],
+ * dx [T,d]. T == 0: MOE_OK, nothing touched. */
+int moe_dispatch_bwd(const moe_shape_t *shape, const void *dx_rows, const int32_t *dest_rank,
+                     const int32_t *dest_row, void *dx, hipStream_t stream);
+
+/* Router backward: the gradient of the logits through the softmax over the
+ * K selected logits that produced topk_w (Sec. 05, Fig. 15); the selection
+ * itself is piecewise constant and passes no gradient:
+ *   dlogits[t, topk_idx[t,k]] = topk_w[t,k] * (dw[t,k] - sum_j topk_w[t,j] dw[t,j])
+ * and 0 on every expert token t did not select. topk_idx, topk_w as moe_route
+ * wrote them, dw from moe_combine_bwd; dlogits [T,N] fp32 is fully written.
+ * T == 0: MOE_OK, nothing touched. */
+int moe_route_bwd(const moe_shape_t *shape, const int32_t *topk_idx, const float *topk_w,
+                  const float *dw, float *dlogits, hipStream_t stream);
 
 /* Human-readable text of a return code (static storage, never NULL). */
 const char *moe_strerror(int code);

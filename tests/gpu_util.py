@@ -62,6 +62,52 @@ def assert_rows_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str) -
     return worst
 
 
+def assert_bounded(got: np.ndarray, ref: np.ndarray, scale: np.ndarray, tol: float,
+                   what: str) -> float:
+    """|got - ref| <= tol * scale elementwise, where ``scale`` is the
+    Cauchy-Schwarz bound of the quantity (e.g. ||a|| ||b|| for a dot product
+    <a, b>): a relative error tol on the operands moves the result by at most
+    that much, however much the dot product itself cancels. Entries whose
+    scale is zero must match exactly. Returns the worst |got-ref|/scale."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = np.asarray(scale, dtype=np.float64)
+    assert got.shape == ref.shape == scale.shape, (what, got.shape, ref.shape, scale.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    zero = scale == 0
+    assert np.all(got[zero] == ref[zero]), f"{what}: entries with a zero bound differ"
+    if not np.any(~zero):
+        return 0.0
+    r = np.abs(got[~zero] - ref[~zero]) / scale[~zero]
+    worst = float(r.max())
+    assert worst <= tol, f"{what}: worst error / bound {worst:.3e} > {tol:.1e}"
+    return worst
+
+
+def dw_bound(dout: np.ndarray, y: np.ndarray, dest_rank, dest_row, ep_rank: int) -> np.ndarray:
+    """||dout[t]|| * ||y[dest_row[t,k]]|| for the kept local routes, else 0."""
+    T, K = dest_rank.shape
+    b = np.zeros((T, K))
+    dn = np.linalg.norm(np.asarray(dout, dtype=np.float64), axis=1)
+    for t in range(T):
+        for k in range(K):
+            if dest_rank[t, k] == ep_rank:
+                b[t, k] = dn[t] * np.linalg.norm(np.asarray(y[int(dest_row[t, k])], np.float64))
+    return b
+
+
+def dlogit_bound(idx, w, dwb, N: int) -> np.ndarray:
+    """Bound on the logit-gradient error implied by errors dwb on dw:
+    |d dl[t, idx_k]| <= w_k (dwb_k + sum_j w_j dwb_j)."""
+    T, K = idx.shape
+    b = np.zeros((T, N))
+    for t in range(T):
+        inner = float(np.dot(w[t], dwb[t]))
+        for k in range(K):
+            b[t, idx[t, k]] = w[t, k] * (dwb[t, k] + inner)
+    return b
+
+
 def route_gpu(shape: moe.MoeShape, logits_dev: torch.Tensor, row_src: bool = True):
     out = moe.RouteOut.empty(shape, "cuda", row_src=row_src)
     for t in (out.topk_idx, out.dest_rank, out.dest_row, out.counts, out.offsets):

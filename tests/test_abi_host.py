@@ -88,3 +88,24 @@ def test_python_binding_checks_shapes_before_calling():
     s = moe.MoeShape(**BASE)
     with pytest.raises(ValueError):
         moe.moe_dispatch_rows(s, torch.zeros(3, 3), None, None, None)
+
+
+def test_backward_entry_points_validate_on_the_host():
+    lib = _abi.load()
+    good = moe.MoeShape(**BASE).c()
+    assert lib.moe_combine_bwd(ctypes.byref(good), 16, 16, 16, 16, 16, 8, 16, None) == _abi.MOE_EALIGN
+    # 11 pointers then the stream: a NULL dw_down
+    assert lib.moe_expert_ffn_bwd(ctypes.byref(good), *([16] * 10), None, None) == _abi.MOE_EALIGN
+    assert lib.moe_expert_ffn_bwd(ctypes.byref(good), *([16] * 9), 8, 16, None) == _abi.MOE_EALIGN
+    assert lib.moe_dispatch_bwd(ctypes.byref(good), None, 16, 16, 16, None) == _abi.MOE_EALIGN
+    assert lib.moe_route_bwd(ctypes.byref(good), 16, 16, 16, 2, None) == _abi.MOE_EALIGN
+    bad = moe.MoeShape(**{**BASE, "K": 0}).c()
+    assert lib.moe_route_bwd(ctypes.byref(bad), 16, 16, 16, 16, None) == _abi.MOE_EINVAL
+    assert lib.moe_expert_ffn_bwd(ctypes.byref(bad), *([16] * 11), None) == _abi.MOE_EINVAL
+    f32 = moe.MoeShape(**{**BASE, "dtype": "f32"}).c()
+    assert lib.moe_combine_bwd(ctypes.byref(f32), 16, 16, 16, 16, 16, 16, None, None) == _abi.MOE_EALIGN
+    # an empty batch moves nothing in the row and router steps
+    empty = moe.MoeShape(**{**BASE, "T": 0}).c()
+    assert lib.moe_combine_bwd(ctypes.byref(empty), *([None] * 7), None) == 0
+    assert lib.moe_dispatch_bwd(ctypes.byref(empty), None, None, None, None, None) == 0
+    assert lib.moe_route_bwd(ctypes.byref(empty), None, None, None, None, None) == 0
