@@ -31,12 +31,13 @@
 // G, U are recomputed by the forward NT GEMM (no activation, 2F columns);
 // dispatch backward is the forward combine kernel with unit weights.
 #include "moe_internal.h"
+#include "gemm_common.h"
 
 namespace moe {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -203,7 +204,13 @@ struct GemmArgs {
 template <int MODE>
 __device__ __forceinline__ bool get_work(const GemmArgs &p, int tm, int tn, Work &w) {
   if constexpr (MODE == BW_WG) {
-    const int b = blockIdx.x;
+    // tiles numbered expert by expert (n fastest); XCD-aware order as above,
+    // so each XCD works through whole experts and their rows stay in its L2
+    const int total = p.E_L * p.m_tiles * p.n_tiles_n;
+    const int q = (total + kNumXcd - 1) / kNumXcd;
+    const int slot = blockIdx.x / kNumXcd;
+    const int b = (blockIdx.x % kNumXcd) * q + slot;
+    if (slot >= q || b >= total) return false;
     w.expert = b / (p.m_tiles * p.n_tiles_n);
     w.m0 = ((b / p.n_tiles_n) % p.m_tiles) * tm;
     w.n0 = (b % p.n_tiles_n) * tn;
@@ -385,6 +392,336 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bwd(GemmArgs p) {
       }
 }
 
+// ---- bf16 big tiles: the forward's pipeline for operands of any layout.
+// 256 x 256 block tile, K step 64, two LDS stages, 8 waves of 128 x 64 (4 x 2
+// MFMA 32x32x16 tiles each), operands loaded global -> LDS directly and the
+// loads of step k+1 issued between the MFMAs of step k (as in the forward).
+// Two LDS tile layouts per stage (32 KiB per operand):
+//   K-contiguous (A of DH, DX): 256 rows of 64 k (128 B), chunk-swizzled as in
+//     the forward, fragments read with ds_read_b128;
+//   MN-contiguous (B always, A of WG): 64 k-rows of 256 m or n (512 B); the
+//     16-byte chunk c of k-row r is stored at c ^ 4*(r % 4). Fragments are read
+//     with the LDS transpose read ds_read_b64_tr_b16: in each 16-lane group,
+//     lane 4j+a points at k-row j, columns 4a..4a+3 of the group's 16
+//     columns, and lane i receives column i of the four k-rows. Two such reads
+//     (k-rows +0..3, +4..7) give a lane its 8 k-values; the swizzle puts the
+//     4 k-rows x 4 chunks that two 16-lane groups read at once in 16 distinct
+//     16-byte bank groups.
+// Weight gradients contract over a ragged row range: loads clamp the row to
+// the expert's last one (in bounds, finite) and the last partial step zeroes
+// the B rows past the range in LDS before its MFMAs.
+namespace bt {
+constexpr int BM = 256, BN = 256, BK = 64, NW = 8, NT = 64 * NW;
+constexpr int TM = 4, TN = 2;          // 32 x 32 MFMA tiles per wave
+constexpr int KROW = BK * 2;           // bytes per row of a K-contiguous tile
+constexpr int MNROW = 256 * 2;         // bytes per k-row of an MN-contiguous tile
+constexpr int TILE = 32768;            // bytes per operand tile
+constexpr int STAGE = 2 * TILE;
+constexpr int LPW = 4;                 // direct loads per wave per operand per step
+constexpr int KS = BK / 16;            // MFMA K sub-steps per step
+}  // namespace bt
+
+struct BigCtx {
+  const uint16_t *A, *Bj;
+  int lda, ldb, kbeg, kend;
+  uint32_t a_off[bt::LPW];   // K-contiguous A: element offset of (clamped row, chunk)
+  int a_col[bt::LPW];        // MN-contiguous A: column (clamped)
+  int b_col[bt::LPW];        // B: column (clamped)
+  int krow[bt::LPW];         // MN-contiguous tiles: k-row of each load within the step
+  int fa[bt::TM], fb[bt::TN];
+  int sw;
+};
+
+__device__ __forceinline__ bf16x8_t tr_pair(const uint8_t *p) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * bt::MNROW));
+  const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <int MODE>
+__device__ __forceinline__ const uint16_t *big_a_src(const BigCtx &c, int i, int k0) {
+  if constexpr (MODE == BW_WG) {
+    const int row = min(c.kbeg + k0 + c.krow[i], c.kend - 1);
+    return c.A + (size_t)row * c.lda + c.a_col[i];
+  } else {
+    return c.A + c.a_off[i] + k0;
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ const uint16_t *big_b_src(const BigCtx &c, int i, int k0) {
+  int row = c.kbeg + k0 + c.krow[i];
+  if constexpr (MODE == BW_WG) row = min(row, c.kend - 1);
+  return c.Bj + (size_t)row * c.ldb + c.b_col[i];
+}
+
+template <int MODE>
+__device__ __forceinline__ void big_issue(const BigCtx &c, int k0, int wv,
+                                          uint8_t *__restrict__ stage) {
+#pragma unroll
+  for (int i = 0; i < bt::LPW; ++i)
+    __builtin_amdgcn_global_load_lds(big_a_src<MODE>(c, i, k0),
+                                     MOE_LDS(stage + (wv * bt::LPW + i) * 1024), 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < bt::LPW; ++i)
+    __builtin_amdgcn_global_load_lds(big_b_src<MODE>(c, i, k0),
+                                     MOE_LDS(stage + bt::TILE + (wv * bt::LPW + i) * 1024), 16,
+                                     0, 0);
+}
+
+// One main-loop step (see the forward's big_step): MFMAs of this step from
+// `rd`, one direct load of the next step into `ld` every other MFMA over the
+// first half, fragments double-buffered across the K sub-steps.
+template <int MODE>
+__device__ __forceinline__ void big_step(const BigCtx &c, int k0, bool do_load, int wv,
+                                         uint8_t *__restrict__ ld, const uint8_t *__restrict__ rd,
+                                         int khalf, f32x16_t (&acc)[bt::TM][bt::TN]) {
+  constexpr int MF = bt::KS * bt::TM * bt::TN;   // 32 MFMAs per step
+  constexpr int L = 2 * bt::LPW;                 // 8 direct loads per step
+  constexpr int GAP = MF / (2 * L);
+  auto issue_one = [&](int d) {
+    if (d < bt::LPW)
+      __builtin_amdgcn_global_load_lds(big_a_src<MODE>(c, d, k0),
+                                       MOE_LDS(ld + (wv * bt::LPW + d) * 1024), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(big_b_src<MODE>(c, d - bt::LPW, k0),
+                                       MOE_LDS(ld + bt::TILE + (wv * bt::LPW + d - bt::LPW) * 1024),
+                                       16, 0, 0);
+  };
+  bf16x8_t fra[2][bt::TM], frb[2][bt::TN];
+  auto read_frag = [&](int buf, int ks, int q) {
+    if (q < bt::TM) {
+      if constexpr (MODE == BW_WG)
+        fra[buf][q] = tr_pair(rd + c.fa[q] + ks * 16 * bt::MNROW);
+      else
+        fra[buf][q] = *reinterpret_cast<const bf16x8_t *>(
+            rd + c.fa[q] + (((ks * 2 + khalf) ^ c.sw) << 4));
+    } else {
+      frb[buf][q - bt::TM] = tr_pair(rd + bt::TILE + c.fb[q - bt::TM] + ks * 16 * bt::MNROW);
+    }
+  };
+#pragma unroll
+  for (int q = 0; q < bt::TM + bt::TN; ++q) read_frag(0, 0, q);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < bt::KS; ++ks) {
+    const int cur = ks & 1;
+#pragma unroll
+    for (int q = 0; q < bt::TM * bt::TN; ++q) {
+      const int g = ks * bt::TM * bt::TN + q;
+      const int i = q / bt::TN, j = q % bt::TN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fra[cur][i], frb[cur][j], acc[i][j],
+                                                          0, 0, 0);
+      if (ks + 1 < bt::KS && q < bt::TM + bt::TN) read_frag(cur ^ 1, ks + 1, q);
+      if (do_load && g % GAP == 0 && g / GAP < L) issue_one(g / GAP);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(bt::NT, 1) void k_gemm_bwd_big(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * bt::STAGE];
+  Work wk;
+  if (!get_work<MODE>(p, bt::BM, bt::BN, wk)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int wm = wv >> 2, wn = wv & 3;
+  const int khalf = lane >> 5, fr = lane & 31;
+
+  BigCtx c;
+  c.A = static_cast<const uint16_t *>(p.A);
+  c.Bj = static_cast<const uint16_t *>(p.B) +
+         (MODE == BW_WG ? 0 : (int64_t)wk.expert * p.b_expert_stride);
+  c.lda = p.lda;
+  c.ldb = p.ldb;
+  c.kbeg = wk.kbeg;
+  c.kend = wk.kend;
+  const int a_cols = MODE == BW_WG ? p.M : 0;
+  {
+    // MN-contiguous loads: 2 k-rows of 32 chunks per instruction
+    const int pch = lane & 31;
+#pragma unroll
+    for (int i = 0; i < bt::LPW; ++i) {
+      const int kr = 2 * (wv * bt::LPW + i) + (lane >> 5);
+      const int cl = pch ^ (4 * (kr & 3));
+      c.krow[i] = kr;
+      c.b_col[i] = min(wk.n0 + 8 * cl, p.N - 8);
+      c.a_col[i] = min(wk.m0 + 8 * cl, a_cols - 8);
+    }
+    // K-contiguous A: 8 rows of 8 chunks per instruction
+    const int lrow = lane >> 3, kch = lane & 7;
+#pragma unroll
+    for (int i = 0; i < bt::LPW; ++i) {
+      const int r = (wv * bt::LPW + i) * 8 + lrow;
+      const int grow = min(wk.m0 + r, wk.m_end - 1);   // clamped rows are discarded
+      c.a_off[i] = (uint32_t)grow * (uint32_t)p.lda + ((kch ^ chunk_swz<8>(r)) << 3);
+    }
+  }
+  {
+    // transpose-read fragment offsets: lane 4j+a of 16-lane group g
+    const int g = lane >> 4, j = (lane >> 2) & 3, a = lane & 3;
+    auto mn_off = [&](int col0) {
+      const int cl = ((col0 + (g & 1) * 16 + 4 * a) >> 3) ^ (4 * j);
+      return ((g >> 1) * 8 + j) * bt::MNROW + cl * 16 + (a & 1) * 8;
+    };
+#pragma unroll
+    for (int t = 0; t < bt::TN; ++t) c.fb[t] = mn_off(wn * 64 + t * 32);
+#pragma unroll
+    for (int t = 0; t < bt::TM; ++t)
+      c.fa[t] = MODE == BW_WG ? mn_off(wm * 128 + t * 32) : (wm * 128 + t * 32 + fr) * bt::KROW;
+    c.sw = chunk_swz<8>(fr);
+  }
+
+  f32x16_t acc[bt::TM][bt::TN];
+#pragma unroll
+  for (int i = 0; i < bt::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < bt::TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int klen = wk.kend - wk.kbeg;
+  const int nk = (klen + bt::BK - 1) / bt::BK;
+  const int rem = klen % bt::BK;
+  if (nk > 0) big_issue<MODE>(c, 0, wv, smem);
+  for (int kb = 0; kb < nk; ++kb) {
+    wait_vmcnt<0>();            // this wave's loads of step kb have landed ...
+    __builtin_amdgcn_s_barrier();   // ... and so have every wave's
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    uint8_t *ld = smem + ((kb + 1) & 1) * bt::STAGE;   // read in step kb-1: free now
+    uint8_t *rd = smem + (kb & 1) * bt::STAGE;
+    if (MODE == BW_WG && kb == nk - 1 && rem != 0) {
+      // rows past the expert's range contribute nothing: zero them in B
+      const u32x4_t z = {0, 0, 0, 0};
+      for (int o = rem * bt::MNROW + tid * 16; o < bt::TILE; o += bt::NT * 16)
+        *reinterpret_cast<u32x4_t *>(rd + bt::TILE + o) = z;
+      __syncthreads();
+    }
+    big_step<MODE>(c, (kb + 1) * bt::BK, kb + 1 < nk, wv, ld, rd, khalf, acc);
+  }
+
+  // ---- epilogues. MFMA result layout: register r of lane l holds row
+  // 8*(r/4) + 4*(l/32) + r%4, column l%32 of its 32 x 32 tile.
+  if constexpr (MODE == BW_WG) {
+    float *O = static_cast<float *>(p.Out) + wk.expert * p.out_expert_stride;
+#pragma unroll
+    for (int tm = 0; tm < bt::TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < bt::TN; ++tn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wk.m0 + wm * 128 + tm * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
+          const int col = wk.n0 + wn * 64 + tn * 32 + fr;
+          if (row < p.M && col < p.N) O[(size_t)row * p.ldo + col] = acc[tm][tn][r];
+        }
+  } else if constexpr (MODE == BW_DX) {
+    // bf16 rows through LDS, 16-byte stores (the forward's epilogue): lanes
+    // swap one value with their DPP partner so each writes two adjacent
+    // columns of one row as a dword; chunk c of LDS row r sits at c ^ 4*q(r),
+    // q(r) = bit0(r) | bit2(r) << 1
+    constexpr int ROWB = bt::BN * 2;
+    __syncthreads();
+    auto stage_off = [](int row, int colb) {
+      const int q = (row & 1) | (((row >> 2) & 1) << 1);
+      return row * ROWB + ((((colb >> 4) ^ (q << 2))) << 4) + (colb & 15);
+    };
+    const bool odd = (lane & 1) != 0;
+#pragma unroll
+    for (int tm = 0; tm < bt::TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < bt::TN; ++tn) {
+        const int colb0 = (wn * 64 + tn * 32) * 2;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float v0 = acc[tm][tn][r], v1 = acc[tm][tn][r + 1];
+          const float send = odd ? v0 : v1;
+          const float recv = __int_as_float(
+              __builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
+          const int row = wm * 128 + tm * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3) + (odd ? 1 : 0);
+          const int colb = colb0 + (fr & ~1) * 2;
+          const uint32_t packed = odd ? pack_bf16x2(recv, v1) : pack_bf16x2(v0, recv);
+          *reinterpret_cast<uint32_t *>(smem + stage_off(row, colb)) = packed;
+        }
+      }
+    __syncthreads();
+    constexpr int CPR = ROWB / 16;
+    const int ncols = min(bt::BN, p.N - wk.n0);
+    const int nrows = min(bt::BM, wk.m_end - wk.m0);
+    uint16_t *O = static_cast<uint16_t *>(p.Out);
+#pragma unroll 4
+    for (int idx = tid; idx < bt::BM * CPR; idx += bt::NT) {
+      const int row = idx / CPR, ch = idx % CPR;
+      if (row < nrows && ch * 8 < ncols) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(smem + stage_off(row, ch * 16));
+        *reinterpret_cast<u32x4_t *>(O + (size_t)(wk.m0 + row) * p.ldo + wk.n0 + ch * 8) = v;
+      }
+    }
+  } else {
+    // DH: dH stays fp32; it goes through LDS in two halves of 128 columns
+    // (row pitch 512 B, 16-byte chunk c of row r at c ^ 8*bit2(r)). Each
+    // thread then takes 8 columns of a row, reads G and U of those columns as
+    // 16-byte vectors and writes dG and dU the same way.
+    const int ncols = min(bt::BN, p.N - wk.n0);
+    const int nrows = min(bt::BM, wk.m_end - wk.m0);
+    const uint16_t *GU = static_cast<const uint16_t *>(p.gu);
+    uint16_t *DGU = static_cast<uint16_t *>(p.Out);
+    const size_t ld2 = (size_t)2 * p.F;
+    auto sw_off = [](int row, int col) {   // byte offset of fp32 (row, col) in the half
+      return row * 512 + ((((col >> 2) ^ (((row >> 2) & 1) << 3))) << 4) + (col & 3) * 4;
+    };
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();
+      if ((wn >> 1) == h) {
+#pragma unroll
+        for (int tm = 0; tm < bt::TM; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < bt::TN; ++tn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = wm * 128 + tm * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
+              const int col = (wn & 1) * 64 + tn * 32 + fr;
+              *reinterpret_cast<float *>(smem + sw_off(row, col)) = acc[tm][tn][r];
+            }
+      }
+      __syncthreads();
+      for (int idx = tid; idx < bt::BM * 16; idx += bt::NT) {
+        const int row = idx >> 4, c8 = idx & 15;
+        const int lcol = h * 128 + c8 * 8;
+        if (row >= nrows || lcol >= ncols) continue;
+        const f32x4_t lo = *reinterpret_cast<const f32x4_t *>(smem + sw_off(row, c8 * 8));
+        const f32x4_t hi = *reinterpret_cast<const f32x4_t *>(smem + sw_off(row, c8 * 8 + 4));
+        const size_t base = (size_t)(wk.m0 + row) * ld2 + wk.n0 + lcol;
+        const u32x4_t gv = *reinterpret_cast<const u32x4_t *>(GU + base);
+        const u32x4_t uv = *reinterpret_cast<const u32x4_t *>(GU + base + p.F);
+        u32x4_t dg, du;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float o[2][2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const float dh = (e < 2) ? lo[2 * e + hh] : hi[2 * (e - 2) + hh];
+            const float g = hh ? bf16_hi(gv[e]) : bf16_lo(gv[e]);
+            const float u = hh ? bf16_hi(uv[e]) : bf16_lo(uv[e]);
+            const float s = 1.0f / (1.0f + __expf(-g));
+            o[0][hh] = dh * u * s * (1.0f + g * (1.0f - s));
+            o[1][hh] = dh * g * s;
+          }
+          dg[e] = pack_bf16x2(o[0][0], o[0][1]);
+          du[e] = pack_bf16x2(o[1][0], o[1][1]);
+        }
+        *reinterpret_cast<u32x4_t *>(DGU + base) = dg;
+        *reinterpret_cast<u32x4_t *>(DGU + base + p.F) = du;
+      }
+    }
+  }
+}
+
 // ---- fp32: 64 x 64 tile, K step 16, 4 x 4 outputs per thread
 constexpr int kFT = 64;
 constexpr int kFK = 16;
@@ -450,9 +787,32 @@ __global__ __launch_bounds__(256) void k_gemm_bwd_f32(GemmArgs p) {
     }
 }
 
+// Grid of a grouped GEMM launch: the capacity bound of row tiles (row modes)
+// or every expert's fixed tiles (WG), times the n-tiles, rounded up to the
+// XCD count.
+inline dim3 gemm_grid(int mode, const moe_shape_t &s, int tile, const GemmArgs &p) {
+  const int E_L = s.N / s.ep_size;
+  int64_t tiles;
+  if (mode == BW_WG)
+    tiles = (int64_t)E_L * p.m_tiles * p.n_tiles_n;
+  else
+    tiles = (ceil_div((int64_t)E_L * s.capacity, tile) + E_L) * p.n_tiles_n;
+  return dim3((unsigned)(ceil_div(tiles, kNumXcd) * kNumXcd));
+}
+
+// One grouped product. bf16: the pipelined 256 x 256 kernel when the
+// contraction of a row mode is a multiple of its K step (the weight-gradient
+// contraction may have any length), else the 128 x 128 kernel; fp32: SIMT.
 template <int MODE>
-void launch_mode(bool bf16, dim3 grid, const GemmArgs &p, hipStream_t st) {
-  if (bf16) hipLaunchKernelGGL(k_gemm_bwd<MODE>, grid, dim3(256), 0, st, p);
+void launch_mode(const moe_shape_t &s, GemmArgs p, hipStream_t st) {
+  const bool bf16 = s.dtype == MOE_BF16;
+  const bool big = bf16 && (MODE == BW_WG || p.Kdim % bt::BK == 0);
+  const int tile = big ? bt::BM : bf16 ? kT : kFT;
+  p.n_tiles_n = (int)ceil_div(p.N, tile);
+  p.m_tiles = MODE == BW_WG ? (int)ceil_div(p.M, tile) : 0;
+  const dim3 grid = gemm_grid(MODE, s, tile, p);
+  if (big) hipLaunchKernelGGL(k_gemm_bwd_big<MODE>, grid, dim3(bt::NT), 0, st, p);
+  else if (bf16) hipLaunchKernelGGL(k_gemm_bwd<MODE>, grid, dim3(256), 0, st, p);
   else hipLaunchKernelGGL(k_gemm_bwd_f32<MODE>, grid, dim3(256), 0, st, p);
 }
 
@@ -500,16 +860,10 @@ int launch_expert_ffn_bwd(const moe_shape_t &s, const void *buf, const int32_t *
                           hipStream_t st) {
   const int E_L = s.N / s.ep_size;
   const int d = s.d, F = s.F;
-  const bool bf16 = s.dtype == MOE_BF16;
-  const int tile = bf16 ? kT : kFT;
   const int32_t *off = offsets + (size_t)s.ep_rank * (E_L + 1);
   // 1. [G U] = X W_gu^T over the prefix rows (forward NT GEMM, no activation)
   int rc = launch_gemm_nt(s, buf, w_gu, off, gu, d, 2 * F, st);
   if (rc != MOE_OK) return rc;
-  const int64_t max_m = ceil_div((int64_t)E_L * s.capacity, tile) + E_L;
-  auto row_grid = [&](int ntn) {
-    return dim3((unsigned)(ceil_div(max_m * ntn, kNumXcd) * kNumXcd));
-  };
   GemmArgs p{};
   p.off = off;
   p.E_L = E_L;
@@ -517,26 +871,22 @@ int launch_expert_ffn_bwd(const moe_shape_t &s, const void *buf, const int32_t *
   // 2. dH = dY W_d (K = d, N = F), SwiGLU backward in the epilogue -> [dG dU]
   p.A = dy; p.lda = d; p.B = w_down; p.ldb = F; p.b_expert_stride = (int64_t)d * F;
   p.M = 0; p.N = F; p.Kdim = d; p.gu = gu; p.Out = dgu; p.ldo = 2 * F;
-  p.n_tiles_n = (int)ceil_div(F, tile);
-  launch_mode<BW_DH>(bf16, row_grid(p.n_tiles_n), p, st);
+  launch_mode<BW_DH>(s, p, st);
   if ((rc = launch_status()) != MOE_OK) return rc;
   // 3. dX = [dG dU] W_gu (K = 2F, N = d)
   p.A = dgu; p.lda = 2 * F; p.B = w_gu; p.ldb = d; p.b_expert_stride = (int64_t)2 * F * d;
   p.N = d; p.Kdim = 2 * F; p.gu = nullptr; p.Out = dx_rows; p.ldo = d;
-  p.n_tiles_n = (int)ceil_div(d, tile);
-  launch_mode<BW_DX>(bf16, row_grid(p.n_tiles_n), p, st);
+  launch_mode<BW_DX>(s, p, st);
   if ((rc = launch_status()) != MOE_OK) return rc;
   // 4. dW_d[j] = dY^T H over the expert's rows (M = d, N = F), fp32
   p.A = dy; p.lda = d; p.B = h; p.ldb = F; p.b_expert_stride = 0;
   p.M = d; p.N = F; p.Kdim = 0; p.Out = dw_down; p.ldo = F; p.out_expert_stride = (int64_t)d * F;
-  p.m_tiles = (int)ceil_div(d, tile); p.n_tiles_n = (int)ceil_div(F, tile);
-  launch_mode<BW_WG>(bf16, dim3((unsigned)(E_L * p.m_tiles * p.n_tiles_n)), p, st);
+  launch_mode<BW_WG>(s, p, st);
   if ((rc = launch_status()) != MOE_OK) return rc;
   // 5. dW_gu[j] = [dG dU]^T X over the expert's rows (M = 2F, N = d), fp32
   p.A = dgu; p.lda = 2 * F; p.B = buf; p.ldb = d;
   p.M = 2 * F; p.N = d; p.Out = dw_gu; p.ldo = d; p.out_expert_stride = (int64_t)2 * F * d;
-  p.m_tiles = (int)ceil_div(2 * F, tile); p.n_tiles_n = (int)ceil_div(d, tile);
-  launch_mode<BW_WG>(bf16, dim3((unsigned)(E_L * p.m_tiles * p.n_tiles_n)), p, st);
+  launch_mode<BW_WG>(s, p, st);
   return launch_status();
 }
 

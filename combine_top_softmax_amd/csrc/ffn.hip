@@ -34,12 +34,11 @@
 //     register-staged LDS double buffer with 16-byte row padding.
 // fp32 path: a plain LDS-tiled SIMT kernel (64 x 64 tile, 4 x 4 per thread).
 #include "moe_internal.h"
+#include "gemm_common.h"
 
 namespace moe {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 struct Tile {
   int expert;
@@ -277,21 +276,6 @@ struct BigTile {
   static constexpr int STAGE_BYTES = (BM + BW) * ROW_B;
 };
 
-template <int CH>
-__device__ __forceinline__ int chunk_swz(int r) {
-  if constexpr (CH == 8) return (r & 7) ^ ((r >> 3) & 1);
-  else return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
-}
-
-#define MOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 // Issue the direct global -> LDS loads of one K step into `stage`.
 template <int BM, int BK, int NS, int NW>
