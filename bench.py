@@ -98,12 +98,14 @@ def cpu_baseline(cfg, target_s: float) -> dict:
                       f"BLAS threads={threads}"}
 
 
-BWD_STAGES = ["combine_bwd", "expert_ffn_bwd", "dispatch_bwd", "route_bwd"]
+BWD_STAGES = ["combine_bwd", "expert_ffn_bwd_data", "dispatch_bwd", "route_bwd",
+              "expert_ffn_bwd_weight"]
 
 
 def time_backward(args, layer, inp, stream, torch) -> dict:
-    """Layer backward after the forward's buffers (same route map): four calls
-    per step, timed with events between them. Not part of ``value``."""
+    """Layer backward after the forward's buffers (same route map), in the
+    order MoELayer.backward issues it, timed with events between the calls.
+    Not part of ``value``."""
     from combine_top_softmax_amd.workloads import random_rows
     import combine_top_softmax_amd as moe
     cfg = layer.shape
@@ -117,34 +119,40 @@ def time_backward(args, layer, inp, stream, torch) -> dict:
         moe.moe_combine_bwd(s, dout, layer.y, r.dest_rank, r.dest_row, r.topk_w, layer.dy,
                             layer.dw)
         if ev: ev[1].record(stream)
-        moe.moe_expert_ffn_bwd(s, layer.buf, r.offsets, inp.w_gu, inp.w_d, layer.h, layer.dy,
-                               layer.gu, layer.gu, layer.dx_rows, layer.dw_gu, layer.dw_down)
+        moe.moe_expert_ffn_bwd_data(s, layer.buf, r.offsets, inp.w_gu, inp.w_d, layer.dy,
+                                    layer.gu, layer.gu, layer.dx_rows)
         if ev: ev[2].record(stream)
         moe.moe_dispatch_bwd(s, layer.dx_rows, r.dest_rank, r.dest_row, layer.dx)
         if ev: ev[3].record(stream)
         moe.moe_route_bwd(s, r.topk_idx, r.topk_w, layer.dw, layer.dlogits)
         if ev: ev[4].record(stream)
+        moe.moe_expert_ffn_bwd_weight(s, layer.buf, r.offsets, layer.h, layer.dy, layer.gu,
+                                      layer.dw_gu, layer.dw_down)
+        if ev: ev[5].record(stream)
 
     for _ in range(args.warmup):
         bstep()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.set_sync_debug_mode("error")
     for i in range(args.steps):
         bstep(evs[i])
     torch.cuda.set_sync_debug_mode(0)
     torch.cuda.synchronize()
-    ms = evs[0][0].elapsed_time(evs[-1][4]) / args.steps
+    ms = evs[0][0].elapsed_time(evs[-1][5]) / args.steps
     st = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
           for i, n in enumerate(BWD_STAGES)}
     R = int(r.offsets[s.ep_rank, -1].item())
-    # dH, dX, dW_d, dW_gu: 12 R d F; plus the recomputed [G U]: 4 R d F
-    fl = 12.0 * R * s.d * s.F
-    t_ffn = st["expert_ffn_bwd"] * 1e-3
+    # data half: recomputed [G U] 4 R d F, dH 2 R d F, dX 4 R d F;
+    # weight half: dW_d 2 R d F, dW_gu 4 R d F
+    rdf = float(R) * s.d * s.F
+    t_data, t_wt = st["expert_ffn_bwd_data"] * 1e-3, st["expert_ffn_bwd_weight"] * 1e-3
     return {"ms_per_step": round(ms, 5),
             "stages_ms": {n: round(v, 5) for n, v in st.items()},
-            "expert_ffn_bwd_TFLOPs": round(fl / t_ffn / 1e12, 1),
-            "expert_ffn_bwd_TFLOPs_incl_recompute": round(fl * 16 / 12 / t_ffn / 1e12, 1)}
+            "expert_ffn_bwd_TFLOPs": round(12 * rdf / (t_data + t_wt) / 1e12, 1),
+            "expert_ffn_bwd_TFLOPs_incl_recompute": round(16 * rdf / (t_data + t_wt) / 1e12, 1),
+            "expert_ffn_bwd_data_TFLOPs": round(10 * rdf / t_data / 1e12, 1),
+            "expert_ffn_bwd_weight_TFLOPs": round(6 * rdf / t_wt / 1e12, 1)}
 
 
 def main():

@@ -23,6 +23,7 @@ __all__ = [
     "MoeShape", "RouteOut", "MoELayer", "MoeError", "moe_route_workspace_size", "moe_route",
     "moe_route_map", "moe_dispatch_rows", "moe_expert_ffn", "moe_expert_up",
     "moe_expert_down", "moe_combine", "moe_combine_bwd", "moe_expert_ffn_bwd",
+    "moe_expert_ffn_bwd_data", "moe_expert_ffn_bwd_weight",
     "moe_dispatch_bwd", "moe_route_bwd", "moe_strerror", "moe_validate_shape",
 ]
 
@@ -272,6 +273,39 @@ def moe_expert_ffn_bwd(shape: MoeShape, buf, offsets, w_gu, w_down, h, dy, gu, d
     _abi.check("moe_expert_ffn_bwd", rc)
 
 
+def moe_expert_ffn_bwd_data(shape: MoeShape, buf, offsets, w_gu, w_down, dy, gu, dgu, dx_rows,
+                            stream=None) -> None:
+    dt = shape.torch_dtype
+    _need(buf, "buf", (shape.rows, shape.d), dt)
+    _ffn_checks(shape, offsets)
+    _need(w_gu, "w_gu", (shape.E_L, 2 * shape.F, shape.d), dt)
+    _need(w_down, "w_down", (shape.E_L, shape.d, shape.F), dt)
+    _need(dy, "dy", (shape.rows, shape.d), dt)
+    _need(gu, "gu", (shape.rows, 2 * shape.F), dt)
+    _need(dgu, "dgu", (shape.rows, 2 * shape.F), dt)
+    _need(dx_rows, "dx_rows", (shape.rows, shape.d), dt)
+    rc = _abi.load().moe_expert_ffn_bwd_data(
+        ctypes.byref(shape.c()), _ptr(buf), _ptr(offsets), _ptr(w_gu), _ptr(w_down), _ptr(dy),
+        _ptr(gu), _ptr(dgu), _ptr(dx_rows), _stream(stream))
+    _abi.check("moe_expert_ffn_bwd_data", rc)
+
+
+def moe_expert_ffn_bwd_weight(shape: MoeShape, buf, offsets, h, dy, dgu, dw_gu, dw_down,
+                              stream=None) -> None:
+    dt = shape.torch_dtype
+    _need(buf, "buf", (shape.rows, shape.d), dt)
+    _ffn_checks(shape, offsets)
+    _need(h, "h", (shape.rows, shape.F), dt)
+    _need(dy, "dy", (shape.rows, shape.d), dt)
+    _need(dgu, "dgu", (shape.rows, 2 * shape.F), dt)
+    _need(dw_gu, "dw_gu", (shape.E_L, 2 * shape.F, shape.d), torch.float32)
+    _need(dw_down, "dw_down", (shape.E_L, shape.d, shape.F), torch.float32)
+    rc = _abi.load().moe_expert_ffn_bwd_weight(
+        ctypes.byref(shape.c()), _ptr(buf), _ptr(offsets), _ptr(h), _ptr(dy), _ptr(dgu),
+        _ptr(dw_gu), _ptr(dw_down), _stream(stream))
+    _abi.check("moe_expert_ffn_bwd_weight", rc)
+
+
 def moe_dispatch_bwd(shape: MoeShape, dx_rows, dest_rank, dest_row, dx, stream=None) -> None:
     dt = shape.torch_dtype
     _need(dx_rows, "dx_rows", (shape.rows, shape.d), dt)
@@ -357,8 +391,11 @@ class MoELayer:
         s, r = self.shape, self.route
         moe_combine_bwd(s, dout, self.y, r.dest_rank, r.dest_row, r.topk_w, self.dy, self.dw,
                         stream)
-        moe_expert_ffn_bwd(s, self.buf, r.offsets, w_gu, w_d, self.h, self.dy, self.gu, self.gu,
-                           self.dx_rows, self.dw_gu, self.dw_down, stream)
+        # row gradients first, so dispatch backward reads dX rows while cached
+        moe_expert_ffn_bwd_data(s, self.buf, r.offsets, w_gu, w_d, self.dy, self.gu, self.gu,
+                                self.dx_rows, stream)
         moe_dispatch_bwd(s, self.dx_rows, r.dest_rank, r.dest_row, self.dx, stream)
         moe_route_bwd(s, r.topk_idx, r.topk_w, self.dw, self.dlogits, stream)
+        moe_expert_ffn_bwd_weight(s, self.buf, r.offsets, self.h, self.dy, self.gu, self.dw_gu,
+                                  self.dw_down, stream)
         return self.dx, self.dlogits, self.dw_gu, self.dw_down

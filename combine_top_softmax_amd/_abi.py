@@ -46,6 +46,8 @@ SIGNATURES = {
     "moe_combine": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P]),
     "moe_combine_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_bwd": (ctypes.c_int, [_SHAPE] + [_P] * 12),
+    "moe_expert_ffn_bwd_data": (ctypes.c_int, [_SHAPE] + [_P] * 9),
+    "moe_expert_ffn_bwd_weight": (ctypes.c_int, [_SHAPE] + [_P] * 8),
     "moe_dispatch_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_route_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),

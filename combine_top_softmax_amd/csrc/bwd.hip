@@ -854,10 +854,9 @@ int launch_route_bwd(const moe_shape_t &s, const int32_t *idx, const float *w, c
   return launch_status();
 }
 
-int launch_expert_ffn_bwd(const moe_shape_t &s, const void *buf, const int32_t *offsets,
-                          const void *w_gu, const void *w_down, const void *h, const void *dy,
-                          void *gu, void *dgu, void *dx_rows, float *dw_gu, float *dw_down,
-                          hipStream_t st) {
+int launch_expert_ffn_bwd_data(const moe_shape_t &s, const void *buf, const int32_t *offsets,
+                               const void *w_gu, const void *w_down, const void *dy, void *gu,
+                               void *dgu, void *dx_rows, hipStream_t st) {
   const int E_L = s.N / s.ep_size;
   const int d = s.d, F = s.F;
   const int32_t *off = offsets + (size_t)s.ep_rank * (E_L + 1);
@@ -870,19 +869,31 @@ int launch_expert_ffn_bwd(const moe_shape_t &s, const void *buf, const int32_t *
   p.F = F;
   // 2. dH = dY W_d (K = d, N = F), SwiGLU backward in the epilogue -> [dG dU]
   p.A = dy; p.lda = d; p.B = w_down; p.ldb = F; p.b_expert_stride = (int64_t)d * F;
-  p.M = 0; p.N = F; p.Kdim = d; p.gu = gu; p.Out = dgu; p.ldo = 2 * F;
+  p.N = F; p.Kdim = d; p.gu = gu; p.Out = dgu; p.ldo = 2 * F;
   launch_mode<BW_DH>(s, p, st);
   if ((rc = launch_status()) != MOE_OK) return rc;
   // 3. dX = [dG dU] W_gu (K = 2F, N = d)
   p.A = dgu; p.lda = 2 * F; p.B = w_gu; p.ldb = d; p.b_expert_stride = (int64_t)2 * F * d;
   p.N = d; p.Kdim = 2 * F; p.gu = nullptr; p.Out = dx_rows; p.ldo = d;
   launch_mode<BW_DX>(s, p, st);
-  if ((rc = launch_status()) != MOE_OK) return rc;
+  return launch_status();
+}
+
+int launch_expert_ffn_bwd_weight(const moe_shape_t &s, const void *buf, const int32_t *offsets,
+                                 const void *h, const void *dy, const void *dgu, float *dw_gu,
+                                 float *dw_down, hipStream_t st) {
+  const int E_L = s.N / s.ep_size;
+  const int d = s.d, F = s.F;
+  GemmArgs p{};
+  p.off = offsets + (size_t)s.ep_rank * (E_L + 1);
+  p.E_L = E_L;
+  p.F = F;
   // 4. dW_d[j] = dY^T H over the expert's rows (M = d, N = F), fp32
-  p.A = dy; p.lda = d; p.B = h; p.ldb = F; p.b_expert_stride = 0;
-  p.M = d; p.N = F; p.Kdim = 0; p.Out = dw_down; p.ldo = F; p.out_expert_stride = (int64_t)d * F;
+  p.A = dy; p.lda = d; p.B = h; p.ldb = F;
+  p.M = d; p.N = F; p.Out = dw_down; p.ldo = F; p.out_expert_stride = (int64_t)d * F;
   launch_mode<BW_WG>(s, p, st);
-  if ((rc = launch_status()) != MOE_OK) return rc;
+  int rc = launch_status();
+  if (rc != MOE_OK) return rc;
   // 5. dW_gu[j] = [dG dU]^T X over the expert's rows (M = 2F, N = d), fp32
   p.A = dgu; p.lda = 2 * F; p.B = buf; p.ldb = d;
   p.M = 2 * F; p.N = d; p.Out = dw_gu; p.ldo = d; p.out_expert_stride = (int64_t)2 * F * d;

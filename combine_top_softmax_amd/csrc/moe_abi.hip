@@ -155,18 +155,45 @@ int moe_combine_bwd(const moe_shape_t *shape, const void *dout, const void *y,
   return moe::launch_combine_bwd(*shape, dout, y, dest_rank, dest_row, topk_w, dy, dw, stream);
 }
 
+int moe_expert_ffn_bwd_data(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
+                            const void *w_gu, const void *w_down, const void *dy, void *gu,
+                            void *dgu, void *dx_rows, hipStream_t stream) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!aligned16(buf) || !aligned16(w_gu) || !aligned16(w_down) || !aligned16(dy) ||
+      !aligned16(gu) || !aligned16(dgu) || !aligned16(dx_rows) || !aligned4(offsets))
+    return MOE_EALIGN;
+  return moe::launch_expert_ffn_bwd_data(*shape, buf, offsets, w_gu, w_down, dy, gu, dgu, dx_rows,
+                                         stream);
+}
+
+int moe_expert_ffn_bwd_weight(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
+                              const void *h, const void *dy, const void *dgu, float *dw_gu,
+                              float *dw_down, hipStream_t stream) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!aligned16(buf) || !aligned16(h) || !aligned16(dy) || !aligned16(dgu) ||
+      !aligned16(dw_gu) || !aligned16(dw_down) || !aligned4(offsets))
+    return MOE_EALIGN;
+  return moe::launch_expert_ffn_bwd_weight(*shape, buf, offsets, h, dy, dgu, dw_gu, dw_down,
+                                           stream);
+}
+
 int moe_expert_ffn_bwd(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
                        const void *w_gu, const void *w_down, const void *h, const void *dy,
                        void *gu, void *dgu, void *dx_rows, float *dw_gu, float *dw_down,
                        hipStream_t stream) {
-  const int rc = check_shape(shape);
+  int rc = check_shape(shape);
   if (rc != MOE_OK) return rc;
   if (!aligned16(buf) || !aligned16(w_gu) || !aligned16(w_down) || !aligned16(h) ||
       !aligned16(dy) || !aligned16(gu) || !aligned16(dgu) || !aligned16(dx_rows) ||
       !aligned16(dw_gu) || !aligned16(dw_down) || !aligned4(offsets))
     return MOE_EALIGN;
-  return moe::launch_expert_ffn_bwd(*shape, buf, offsets, w_gu, w_down, h, dy, gu, dgu, dx_rows,
-                                    dw_gu, dw_down, stream);
+  rc = moe::launch_expert_ffn_bwd_data(*shape, buf, offsets, w_gu, w_down, dy, gu, dgu, dx_rows,
+                                       stream);
+  if (rc != MOE_OK) return rc;
+  return moe::launch_expert_ffn_bwd_weight(*shape, buf, offsets, h, dy, dgu, dw_gu, dw_down,
+                                           stream);
 }
 
 int moe_dispatch_bwd(const moe_shape_t *shape, const void *dx_rows, const int32_t *dest_rank,

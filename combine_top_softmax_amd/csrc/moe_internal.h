@@ -43,10 +43,12 @@ int launch_combine_bwd(const moe_shape_t &s, const void *dout, const void *y,
                        float *dw, hipStream_t st);
 int launch_route_bwd(const moe_shape_t &s, const int32_t *idx, const float *w, const float *dw,
                      float *dlogits, hipStream_t st);
-int launch_expert_ffn_bwd(const moe_shape_t &s, const void *buf, const int32_t *offsets,
-                          const void *w_gu, const void *w_down, const void *h, const void *dy,
-                          void *gu, void *dgu, void *dx_rows, float *dw_gu, float *dw_down,
-                          hipStream_t st);
+int launch_expert_ffn_bwd_data(const moe_shape_t &s, const void *buf, const int32_t *offsets,
+                               const void *w_gu, const void *w_down, const void *dy, void *gu,
+                               void *dgu, void *dx_rows, hipStream_t st);
+int launch_expert_ffn_bwd_weight(const moe_shape_t &s, const void *buf, const int32_t *offsets,
+                                 const void *h, const void *dy, const void *dgu, float *dw_gu,
+                                 float *dw_down, hipStream_t st);
 
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;

@@ -176,7 +176,10 @@ int moe_combine(const moe_shape_t *shape, const void *y, const int32_t *dest_ran
  * Sec. 5.6, Table 8: combine backward, dispatch backward and the
  * router-weight gradient run on the same destination rank/row indices as the
  * forward; Sec. 5.7: the expert backward GEMMs cover the packed prefix only).
- * Order: moe_combine_bwd, moe_expert_ffn_bwd, moe_dispatch_bwd, moe_route_bwd.
+ * Order: moe_combine_bwd, moe_expert_ffn_bwd, moe_dispatch_bwd, moe_route_bwd;
+ * or, with the expert backward in its two halves: moe_combine_bwd,
+ * moe_expert_ffn_bwd_data, moe_dispatch_bwd, moe_route_bwd,
+ * moe_expert_ffn_bwd_weight.
  * On an expert shard each call yields the shard's contribution; dx and dlogits
  * of the whole layer are the sums over the ranks.
  * ------------------------------------------------------------------------ */
@@ -212,6 +215,19 @@ int moe_expert_ffn_bwd(const moe_shape_t *shape, const void *buf, const int32_t 
                        const void *w_gu, const void *w_down, const void *h, const void *dy,
                        void *gu, void *dgu, void *dx_rows, float *dw_gu, float *dw_down,
                        hipStream_t stream);
+
+/* The two halves of moe_expert_ffn_bwd, same arguments and layouts:
+ * moe_expert_ffn_bwd_data writes gu, dgu and dx_rows (the row gradients, what
+ * moe_dispatch_bwd needs next); moe_expert_ffn_bwd_weight writes dw_gu and
+ * dw_down from buf, h, dy and the dgu the first half wrote. Issuing the data
+ * half, then moe_dispatch_bwd, then the weight half reads dx_rows while it is
+ * still in cache. */
+int moe_expert_ffn_bwd_data(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
+                            const void *w_gu, const void *w_down, const void *dy, void *gu,
+                            void *dgu, void *dx_rows, hipStream_t stream);
+int moe_expert_ffn_bwd_weight(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
+                              const void *h, const void *dy, const void *dgu, float *dw_gu,
+                              float *dw_down, hipStream_t stream);
 
 /* Dispatch backward (Table 8: each token pulls its route gradients and sums
  * them): dx[t] = sum over k ascending with dest_rank[t,k] == ep_rank of

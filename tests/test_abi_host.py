@@ -109,3 +109,13 @@ def test_backward_entry_points_validate_on_the_host():
     assert lib.moe_combine_bwd(ctypes.byref(empty), *([None] * 7), None) == 0
     assert lib.moe_dispatch_bwd(ctypes.byref(empty), None, None, None, None, None) == 0
     assert lib.moe_route_bwd(ctypes.byref(empty), None, None, None, None, None) == 0
+
+
+def test_backward_halves_validate_on_the_host():
+    lib = _abi.load()
+    good = moe.MoeShape(**BASE).c()
+    assert lib.moe_expert_ffn_bwd_data(ctypes.byref(good), *([16] * 7), None, None) == _abi.MOE_EALIGN
+    assert lib.moe_expert_ffn_bwd_weight(ctypes.byref(good), *([16] * 6), None, None) == _abi.MOE_EALIGN
+    bad = moe.MoeShape(**{**BASE, "F": 12}).c()
+    assert lib.moe_expert_ffn_bwd_data(ctypes.byref(bad), *([16] * 8), None) == _abi.MOE_EINVAL
+    assert lib.moe_expert_ffn_bwd_weight(ctypes.byref(bad), *([16] * 7), None) == _abi.MOE_EINVAL

@@ -96,9 +96,10 @@ def test_expert_ffn_bwd_matches_oracle(cfg):
     assert_rows_close(to_np(dw_d).reshape(-1, F), r["dw_d"].reshape(-1, F), tol, "dw_down")
 
 
-@pytest.mark.parametrize("cfg", SMALL[:3], ids=lambda c: c.name)
-def test_expert_ffn_bwd_in_place(cfg):
-    """dgu may be the same buffer as gu: same results as separate buffers."""
+@pytest.mark.parametrize("cfg", SMALL[:3] + SMALL[6:7], ids=lambda c: c.name)
+def test_expert_ffn_bwd_variants_agree(cfg):
+    """Separate [G U] and [dG dU] buffers, dgu == gu in place, and the data
+    and weight halves called one after the other all give the same bits."""
     inp = make_inputs(cfg, "cpu")
     ref = oracle_route(cfg, inp.logits)
     shape = moe.MoeShape.from_config(cfg)
@@ -108,19 +109,25 @@ def test_expert_ffn_bwd_in_place(cfg):
     h = random_rows(rows, F, dt, seed=cfg.seed + 601).cuda()
     dy = random_rows(rows, d, dt, seed=cfg.seed + 602).cuda()
     off = _dev(ref["offsets"])
+    w_gu, w_d = inp.w_gu.cuda(), inp.w_d.cuda()
     outs = []
-    for in_place in (False, True):
+    for variant in ("separate", "in_place", "halves"):
         gu = torch.zeros(rows, 2 * F, dtype=dt, device="cuda")
-        dgu = gu if in_place else torch.zeros(rows, 2 * F, dtype=dt, device="cuda")
+        dgu = torch.zeros(rows, 2 * F, dtype=dt, device="cuda") if variant == "separate" else gu
         dx_rows = torch.zeros(rows, d, dtype=dt, device="cuda")
         dw_gu = torch.zeros(E_L, 2 * F, d, dtype=torch.float32, device="cuda")
         dw_d = torch.zeros(E_L, d, F, dtype=torch.float32, device="cuda")
-        w_gu, w_d = inp.w_gu.cuda(), inp.w_d.cuda()
-        moe.moe_expert_ffn_bwd(shape, buf, off, w_gu, w_d, h, dy, gu, dgu, dx_rows, dw_gu, dw_d)
-        outs.append((dgu.clone(), dx_rows, dw_gu, dw_d))
+        if variant == "halves":
+            moe.moe_expert_ffn_bwd_data(shape, buf, off, w_gu, w_d, dy, gu, dgu, dx_rows)
+            moe.moe_expert_ffn_bwd_weight(shape, buf, off, h, dy, dgu, dw_gu, dw_d)
+        else:
+            moe.moe_expert_ffn_bwd(shape, buf, off, w_gu, w_d, h, dy, gu, dgu, dx_rows, dw_gu,
+                                   dw_d)
+        outs.append((dgu, dx_rows, dw_gu, dw_d))
     torch.cuda.synchronize()
-    for a, b in zip(*outs):
-        assert torch.equal(a, b)
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
