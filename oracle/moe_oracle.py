@@ -22,6 +22,13 @@ with rowwise dispatch, as the pages describe it:
   * Backward: Olmo-core MoE report Sec. 5.6 Table 8 (adjoint row movements
     sharing the saved route map, router-weight gradient from the gathered
     expert outputs) and Sec. 5.7 (weight-gradient GEMMs over the valid prefix).
+  * MXFP8 forward: Olmo-core MoE report Sec. 5.5 (rows quantized during
+    dispatch; the grouped GEMM consumes the quantized data and scales
+    directly), Sec. 5.8 (an MXFP8 route carries a qdata row and a scale row
+    that follow the same destination indices and validity mask), Sec. 5.9
+    (E4M3 data with E8M0 scales on forward dispatch, MXFP8 expert GEMMs,
+    forward combine in BF16). The block format is the OCP microscaling (MX)
+    format the report cites; see the MXFP8 section below.
 
 Arithmetic is float64; values are rounded once to the layer's storage type at
 the points where the layer stores them (routing weights -> fp32; expert hidden
@@ -53,6 +60,8 @@ __all__ = [
     "silu", "expert_ffn", "expert_ffn_rows", "combine", "combine_tokens",
     "moe_layer", "local_offsets", "combine_bwd", "expert_ffn_bwd_rows", "expert_ffn_bwd",
     "dispatch_bwd", "route_bwd", "moe_layer_bwd",
+    "E4M3_MAX", "e4m3_decode", "e4m3_encode", "e8m0_decode", "mx_quantize", "mx_dequantize",
+    "dispatch_mx", "expert_ffn_mx_rows", "expert_ffn_mx", "moe_layer_mx",
 ]
 
 
@@ -462,4 +471,179 @@ def moe_layer_bwd(fwd: dict, dout, x, w_gu, w_d, K: int, C: int, ep_size: int, e
     dl = route_bwd(fwd["topk_idx"], fwd["topk_w"], dw, N)
     res = dict(ffn)
     res.update(dy=dy, dw=dw, dx_rows=ffn["dx"], dx=dx, dlogits=dl)
+    return res
+
+
+# --------------------------------------------------------------------------
+# MXFP8 forward
+# --------------------------------------------------------------------------
+# Olmo-core MoE report, Sec. 5.5 / 5.8 / 5.9: forward dispatch moves E4M3
+# data with E8M0 scales, the expert GEMMs consume them directly, combine stays
+# BF16. The block format is the OCP microscaling format the report cites
+# (Rouhani et al. 2023; Open Compute Project 2023), read here as:
+#   * a block is 32 consecutive elements along the contraction dimension of a
+#     GEMM operand (the contiguous dimension of x rows, H rows and of the
+#     [out, in] expert weights);
+#   * the block's shared scale is X = 2^(floor(log2(amax)) - 8), amax the
+#     largest magnitude in the block and 8 the exponent of E4M3's largest
+#     normal (448 = 1.75 * 2^8); it is stored as an E8M0 code (biased exponent
+#     127, clamped to [0, 254]); an all-zero block gets code 0;
+#   * each element is V / X rounded to the nearest E4M3 value, ties to the
+#     even code, magnitudes past the largest normal saturating to 448; the sign
+#     bit follows the sign of V (so -0.0 and negative values that round to
+#     zero give code 0x80).
+# Where the pages leave the MX path open it mirrors the BF16 path: H is
+# computed in float64, rounded to bf16, then quantized along F for the down
+# GEMM; Y is rounded to bf16; combine is the BF16 combine.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code) -> np.ndarray:
+    """Value of OCP E4M3 (FN variant) codes: 1 sign bit, 4 exponent bits with
+    bias 7, 3 mantissa bits; exponent field 0 holds subnormals m/8 * 2^-6;
+    S.1111.111 is NaN; there are no infinities. Returns float64."""
+    c = np.asarray(code).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7))
+    val = np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+    return s * val
+
+
+# the 127 finite non-negative E4M3 values, code order == value order
+_E4M3_POS = e4m3_decode(np.arange(127))
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest E4M3 code to each finite value (ties to the even code),
+    magnitudes past 448 saturating to 448. Returns uint8."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    hi = np.searchsorted(_E4M3_POS, a, side="left")          # first value >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _E4M3_POS[lo]
+    dhi = _E4M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    sign = np.signbit(v)
+    return (code | np.where(sign, 0x80, 0)).astype(np.uint8)
+
+
+def e8m0_decode(code) -> np.ndarray:
+    """2^(code - 127) (code 255 is NaN). Returns float64."""
+    c = np.asarray(code).astype(np.float64)
+    return np.where(c == 255, np.nan, np.exp2(c - 127.0))
+
+
+def mx_quantize(v: np.ndarray, block: int = 32):
+    """MX quantization of each row of ``v`` [rows, n] along the row in blocks of
+    ``block`` elements. Returns (qdata [rows, n] uint8 E4M3 codes,
+    scales [rows, n/block] uint8 E8M0 codes)."""
+    v = np.asarray(v, dtype=np.float64)
+    rows, n = v.shape
+    assert n % block == 0
+    vb = v.reshape(rows, n // block, block)
+    amax = np.max(np.abs(vb), axis=2)
+    # floor(log2(amax)) exactly: amax = f * 2^ex with f in [0.5, 1)
+    _, ex = np.frexp(amax)
+    shared = np.where(amax > 0, ex - 1 - 8, -127)
+    shared = np.clip(shared, -127, 127)
+    scales = (shared + 127).astype(np.uint8)
+    q = e4m3_encode(vb / np.exp2(shared.astype(np.float64))[:, :, None])
+    return q.reshape(rows, n), scales
+
+
+def mx_dequantize(q: np.ndarray, scales: np.ndarray, block: int = 32) -> np.ndarray:
+    """E4M3 value times the block's E8M0 scale. Returns float64 [rows, n]."""
+    q = np.asarray(q)
+    rows, n = q.shape
+    x = e4m3_decode(q).reshape(rows, n // block, block)
+    return (x * e8m0_decode(scales)[:, :, None]).reshape(rows, n)
+
+
+def dispatch_mx(x, dest_rank, dest_row, ep_rank: int, n_rows: int):
+    """Quantize-on-dispatch: every token row of x is MX-quantized along d and
+    its qdata and scale rows are copied to each kept local route's capacity
+    row (Sec. 5.8: both follow the route's destination indices and validity
+    mask). Returns (qdata [n_rows, d] uint8, scales [n_rows, d/32] uint8,
+    written [n_rows] bool)."""
+    q, sc = mx_quantize(np.asarray(x, dtype=np.float64))
+    T, K = dest_rank.shape
+    qb = np.zeros((n_rows, q.shape[1]), dtype=np.uint8)
+    sb = np.zeros((n_rows, sc.shape[1]), dtype=np.uint8)
+    written = np.zeros(n_rows, dtype=bool)
+    for t in range(T):
+        for k in range(K):
+            if dest_rank[t, k] == ep_rank and dest_row[t, k] >= 0:
+                r = int(dest_row[t, k])
+                qb[r] = q[t]
+                sb[r] = sc[t]
+                written[r] = True
+    return qb, sb, written
+
+
+def expert_ffn_mx_rows(Xq, Xs, gu_q, gu_s, d_q, d_s):
+    """SwiGLU MLP of one expert on MXFP8 operands: the float64 products of the
+    dequantized operands; H = silu(G) * U rounded to bf16 and MX-quantized
+    along F for the down projection; Y rounded to bf16.
+    Xq/Xs: rows' qdata/scales along d; gu_q/gu_s: W_gu[j] [2F, d] quantized
+    along d; d_q/d_s: W_d[j] [d, F] quantized along F.
+    Returns (Hq, Hs, Y) with Y float64 holding bf16 values."""
+    X = mx_dequantize(Xq, Xs)
+    W = mx_dequantize(gu_q, gu_s)
+    F = W.shape[0] // 2
+    G = X @ W[:F].T
+    U = X @ W[F:].T
+    H = round_bf16(silu(G) * U)
+    Hq, Hs = mx_quantize(H)
+    Y = round_bf16(mx_dequantize(Hq, Hs) @ mx_dequantize(d_q, d_s).T)
+    return Hq, Hs, Y
+
+
+def expert_ffn_mx(qbuf, sbuf, offsets_local, gu_q, gu_s, d_q, d_s):
+    """Grouped MXFP8 expert FFN over each local expert's rows [off[j], off[j+1]).
+    gu_q [E_L, 2F, d], gu_s [E_L, 2F, d/32], d_q [E_L, d, F], d_s [E_L, d, F/32].
+    Returns (Hq [rows, F], Hs [rows, F/32], Y [rows, d] float64, NaN past the prefix)."""
+    E_L = len(offsets_local) - 1
+    rows = qbuf.shape[0]
+    F = gu_q.shape[1] // 2
+    d = d_q.shape[1]
+    Hq = np.zeros((rows, F), dtype=np.uint8)
+    Hs = np.zeros((rows, F // 32), dtype=np.uint8)
+    Y = np.full((rows, d), np.nan)
+    for j in range(E_L):
+        a, b = int(offsets_local[j]), int(offsets_local[j + 1])
+        if b > a:
+            Hq[a:b], Hs[a:b], Y[a:b] = expert_ffn_mx_rows(qbuf[a:b], sbuf[a:b], gu_q[j], gu_s[j],
+                                                          d_q[j], d_s[j])
+    return Hq, Hs, Y
+
+
+def moe_layer_mx(logits, x, w_gu, w_d, K: int, C: int, ep_size: int, ep_rank: int):
+    """The MXFP8 forward of a bf16 layer: routing as moe_layer, quantize-on-
+    dispatch, expert weights MX-quantized along their contraction dimension,
+    the MXFP8 grouped FFN, and the BF16 combine. Returns a dict."""
+    idx, w = topk_softmax(logits, K)
+    N = logits.shape[1]
+    rm = route_map(idx, N, ep_size, C, ep_rank)
+    E_L = N // ep_size
+    n_rows = E_L * C
+    x = np.asarray(x, dtype=np.float64)
+    w_gu = np.asarray(w_gu, dtype=np.float64)
+    w_d = np.asarray(w_d, dtype=np.float64)
+    d = x.shape[1]
+    F = w_gu.shape[1] // 2
+    qbuf, sbuf, written = dispatch_mx(x, rm["dest_rank"], rm["dest_row"], ep_rank, n_rows)
+    gq, gs = mx_quantize(w_gu.reshape(-1, d))
+    dq, ds = mx_quantize(w_d.reshape(-1, F))
+    gq, gs = gq.reshape(E_L, 2 * F, d), gs.reshape(E_L, 2 * F, d // 32)
+    dq, ds = dq.reshape(E_L, d, F), ds.reshape(E_L, d, F // 32)
+    Hq, Hs, Y = expert_ffn_mx(qbuf, sbuf, rm["offsets"][ep_rank], gq, gs, dq, ds)
+    out = combine(Y, rm["dest_rank"], rm["dest_row"], w, ep_rank, "bf16")
+    res = dict(rm)
+    res.update(topk_idx=idx, topk_w=w, qbuf=qbuf, sbuf=sbuf, written=written, w_gu_q=gq,
+               w_gu_s=gs, w_d_q=dq, w_d_s=ds, h_q=Hq, h_s=Hs, y=Y, out=out)
     return res
