@@ -24,7 +24,8 @@ __all__ = [
     "moe_route_map", "moe_dispatch_rows", "moe_expert_ffn", "moe_expert_up",
     "moe_expert_down", "moe_combine", "moe_combine_bwd", "moe_expert_ffn_bwd",
     "moe_expert_ffn_bwd_data", "moe_expert_ffn_bwd_weight",
-    "moe_dispatch_bwd", "moe_route_bwd", "moe_strerror", "moe_validate_shape",
+    "moe_dispatch_bwd", "moe_route_bwd", "moe_mx_quantize_rows", "moe_dispatch_rows_mx",
+    "moe_expert_up_mx", "moe_expert_down_mx", "MxWeights", "moe_strerror", "moe_validate_shape",
 ]
 
 
@@ -327,6 +328,86 @@ def moe_route_bwd(shape: MoeShape, topk_idx, topk_w, dw, dlogits, stream=None) -
     _abi.check("moe_route_bwd", rc)
 
 
+# ----------------------------------------------------------------- MXFP8
+def moe_mx_quantize_rows(src, qdata, scales, stream=None) -> None:
+    """MX-quantize the rows of a bf16 tensor along its last dimension (a
+    multiple of 32): qdata uint8 of src's shape, scales uint8 [..., cols/32]."""
+    if not isinstance(src, torch.Tensor) or src.dtype != torch.bfloat16 or src.dim() < 1:
+        raise ValueError("src must be a bf16 tensor")
+    cols = src.shape[-1]
+    rows = src.numel() // cols if cols else 0
+    _need(src, "src", tuple(src.shape), torch.bfloat16)
+    _need(qdata, "qdata", tuple(src.shape), torch.uint8)
+    _need(scales, "scales", tuple(src.shape[:-1]) + (cols // 32,), torch.uint8)
+    rc = _abi.load().moe_mx_quantize_rows(rows, cols, _ptr(src), _ptr(qdata), _ptr(scales),
+                                          _stream(stream))
+    _abi.check("moe_mx_quantize_rows", rc)
+
+
+def moe_dispatch_rows_mx(shape: MoeShape, x, dest_rank, dest_row, qbuf, sbuf,
+                         stream=None) -> None:
+    _need(x, "x", (shape.T, shape.d), torch.bfloat16)
+    _need(dest_rank, "dest_rank", (shape.T, shape.K), torch.int32)
+    _need(dest_row, "dest_row", (shape.T, shape.K), torch.int32)
+    _need(qbuf, "qbuf", (shape.rows, shape.d), torch.uint8)
+    _need(sbuf, "sbuf", (shape.rows, shape.d // 32), torch.uint8)
+    rc = _abi.load().moe_dispatch_rows_mx(ctypes.byref(shape.c()), _ptr(x), _ptr(dest_rank),
+                                          _ptr(dest_row), _ptr(qbuf), _ptr(sbuf), _stream(stream))
+    _abi.check("moe_dispatch_rows_mx", rc)
+
+
+def moe_expert_up_mx(shape: MoeShape, qbuf, sbuf, offsets, w_gu_q, w_gu_s, h_q, h_s,
+                     stream=None) -> None:
+    u8 = torch.uint8
+    _need(qbuf, "qbuf", (shape.rows, shape.d), u8)
+    _need(sbuf, "sbuf", (shape.rows, shape.d // 32), u8)
+    _ffn_checks(shape, offsets)
+    _need(w_gu_q, "w_gu_q", (shape.E_L, 2 * shape.F, shape.d), u8)
+    _need(w_gu_s, "w_gu_s", (shape.E_L, 2 * shape.F, shape.d // 32), u8)
+    _need(h_q, "h_q", (shape.rows, shape.F), u8)
+    _need(h_s, "h_s", (shape.rows, shape.F // 32), u8)
+    rc = _abi.load().moe_expert_up_mx(ctypes.byref(shape.c()), _ptr(qbuf), _ptr(sbuf),
+                                      _ptr(offsets), _ptr(w_gu_q), _ptr(w_gu_s), _ptr(h_q),
+                                      _ptr(h_s), _stream(stream))
+    _abi.check("moe_expert_up_mx", rc)
+
+
+def moe_expert_down_mx(shape: MoeShape, h_q, h_s, offsets, w_d_q, w_d_s, y, stream=None) -> None:
+    u8 = torch.uint8
+    _need(h_q, "h_q", (shape.rows, shape.F), u8)
+    _need(h_s, "h_s", (shape.rows, shape.F // 32), u8)
+    _ffn_checks(shape, offsets)
+    _need(w_d_q, "w_d_q", (shape.E_L, shape.d, shape.F), u8)
+    _need(w_d_s, "w_d_s", (shape.E_L, shape.d, shape.F // 32), u8)
+    _need(y, "y", (shape.rows, shape.d), torch.bfloat16)
+    rc = _abi.load().moe_expert_down_mx(ctypes.byref(shape.c()), _ptr(h_q), _ptr(h_s),
+                                        _ptr(offsets), _ptr(w_d_q), _ptr(w_d_s), _ptr(y),
+                                        _stream(stream))
+    _abi.check("moe_expert_down_mx", rc)
+
+
+@dataclass
+class MxWeights:
+    """Expert weights quantized once along their contraction dimension."""
+    w_gu_q: torch.Tensor   # [E_L, 2F, d] uint8
+    w_gu_s: torch.Tensor   # [E_L, 2F, d/32] uint8
+    w_d_q: torch.Tensor    # [E_L, d, F] uint8
+    w_d_s: torch.Tensor    # [E_L, d, F/32] uint8
+
+    @classmethod
+    def from_bf16(cls, w_gu: torch.Tensor, w_d: torch.Tensor, stream=None) -> "MxWeights":
+        u8 = torch.uint8
+        E_L, F2, d = w_gu.shape
+        F = F2 // 2
+        q = cls(torch.empty(E_L, F2, d, dtype=u8, device=w_gu.device),
+                torch.empty(E_L, F2, d // 32, dtype=u8, device=w_gu.device),
+                torch.empty(E_L, d, F, dtype=u8, device=w_gu.device),
+                torch.empty(E_L, d, F // 32, dtype=u8, device=w_gu.device))
+        moe_mx_quantize_rows(w_gu, q.w_gu_q, q.w_gu_s, stream)
+        moe_mx_quantize_rows(w_d, q.w_d_q, q.w_d_s, stream)
+        return q
+
+
 # ----------------------------------------------------------------- layer
 class MoELayer:
     """Capacity-shaped buffers allocated once; ``forward`` enqueues the four
@@ -365,6 +446,40 @@ class MoELayer:
         self.dispatch_step(x, stream)
         moe_expert_ffn(self.shape, self.buf, self.route.offsets, w_gu, w_d, self.h, self.y,
                        stream)
+        self.combine_step(stream)
+        return self.out
+
+    def alloc_mx(self, device="cuda") -> None:
+        """MXFP8 forward buffers, allocated once: quantized dispatch rows and
+        the quantized H, each with its scale rows."""
+        s = self.shape
+        u8 = torch.uint8
+        self.qbuf = torch.empty(s.rows, s.d, dtype=u8, device=device)
+        self.sbuf = torch.empty(s.rows, s.d // 32, dtype=u8, device=device)
+        self.h_q = torch.empty(s.rows, s.F, dtype=u8, device=device)
+        self.h_s = torch.empty(s.rows, s.F // 32, dtype=u8, device=device)
+
+    def dispatch_mx_step(self, x, stream=None):
+        r = self.route
+        moe_dispatch_rows_mx(self.shape, x, r.dest_rank, r.dest_row, self.qbuf, self.sbuf, stream)
+
+    def up_mx_step(self, mxw: "MxWeights", stream=None):
+        moe_expert_up_mx(self.shape, self.qbuf, self.sbuf, self.route.offsets, mxw.w_gu_q,
+                         mxw.w_gu_s, self.h_q, self.h_s, stream)
+
+    def down_mx_step(self, mxw: "MxWeights", stream=None):
+        moe_expert_down_mx(self.shape, self.h_q, self.h_s, self.route.offsets, mxw.w_d_q,
+                           mxw.w_d_s, self.y, stream)
+
+    def forward_mx(self, logits, x, mxw: "MxWeights", stream=None) -> torch.Tensor:
+        """MXFP8 forward: the same routing, quantize-on-dispatch, MXFP8 expert
+        GEMMs on the quantized weights, BF16 combine."""
+        if not hasattr(self, "qbuf"):
+            self.alloc_mx(self.out.device)
+        self.route_step(logits, stream)
+        self.dispatch_mx_step(x, stream)
+        self.up_mx_step(mxw, stream)
+        self.down_mx_step(mxw, stream)
         self.combine_step(stream)
         return self.out
 

@@ -50,6 +50,11 @@ SIGNATURES = {
     "moe_expert_ffn_bwd_weight": (ctypes.c_int, [_SHAPE] + [_P] * 8),
     "moe_dispatch_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_route_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
+    "moe_mx_quantize_rows": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]),
+    "moe_dispatch_rows_mx": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_up_mx": (ctypes.c_int, [_SHAPE] + [_P] * 8),
+    "moe_expert_down_mx": (ctypes.c_int, [_SHAPE] + [_P] * 7),
+    "moe_expert_ffn_mx": (ctypes.c_int, [_SHAPE] + [_P] * 11),
     "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_validate_shape": (ctypes.c_int, [_SHAPE]),
 }

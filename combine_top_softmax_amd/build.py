@@ -10,7 +10,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = ["moe_abi.hip", "route.hip", "rows.hip", "ffn.hip", "bwd.hip"]
+SOURCES = ["moe_abi.hip", "route.hip", "rows.hip", "ffn.hip", "bwd.hip", "mx.hip"]
 LIB_NAME = "libmoe_hip.so"
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 

@@ -124,57 +124,6 @@ __global__ __launch_bounds__(256) void k_route_bwd(const int32_t *__restrict__ i
 // ------------------------------------------------------------ grouped GEMMs
 enum { BW_DH = 0, BW_DX = 1, BW_WG = 2 };
 
-struct RowTile {
-  int expert, row0, row_end, n_idx;
-  bool valid;
-};
-
-// Row-grouped modes: the same block -> (expert, m-tile, n-tile) map as the
-// forward grouped GEMM (device offsets, capacity-bound grid, XCD-aware
-// order: block b takes tile (b % 8) * q + b / 8).
-__device__ __forceinline__ RowTile find_row_tile(const int32_t *__restrict__ off, int E_L, int tm,
-                                                 int n_tiles_n) {
-  const int lane = threadIdx.x & 63;
-  RowTile tl;
-  tl.valid = false;
-  int total_m = 0;
-  for (int c = 0; c < E_L; c += 64) {
-    const int j = c + lane;
-    const int n = (j < E_L) ? off[j + 1] - off[j] : 0;
-    const int incl = wave_incl_scan((n + tm - 1) / tm);
-    total_m += __shfl(incl, 63, 64);
-  }
-  const int total = total_m * n_tiles_n;
-  const int q = (total + kNumXcd - 1) / kNumXcd;
-  const int b = blockIdx.x;
-  const int slot = b / kNumXcd;
-  const int L = (b % kNumXcd) * q + slot;
-  if (slot >= q || L >= total) return tl;
-  const int m_glob = L / n_tiles_n;
-  tl.n_idx = L - m_glob * n_tiles_n;
-  int run = 0;
-  for (int c = 0; c < E_L; c += 64) {
-    const int j = c + lane;
-    const int n = (j < E_L) ? off[j + 1] - off[j] : 0;
-    const int mt = (n + tm - 1) / tm;
-    const int incl = wave_incl_scan(mt);
-    const int tot = __shfl(incl, 63, 64);
-    if (m_glob < run + tot) {
-      const uint64_t hit = __ballot(m_glob < run + incl);
-      const int first = __builtin_ctzll(hit);
-      const int excl = __shfl(incl - mt, first, 64);
-      const int e = c + first;
-      tl.expert = e;
-      tl.row0 = off[e] + (m_glob - run - excl) * tm;
-      tl.row_end = off[e + 1];
-      tl.valid = true;
-      return tl;
-    }
-    run += tot;
-  }
-  return tl;
-}
-
 // Problem of one block: expert, output tile origin, valid rows, contraction range.
 struct Work {
   int expert, m0, m_end, n0, kbeg, kend;

@@ -28,4 +28,58 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Row-grouped GEMM tiles from the device offsets of the local experts: the
+// grid is sized from the capacity bound, every block recomputes the
+// per-expert m-tile counts (tm rows each) with a wave scan and maps itself to
+// (expert, m-tile, n-tile) or exits. XCD-aware order: blocks are dealt to the
+// 8 XCDs round-robin, so block b takes tile (b % 8) * q + b / 8 and each XCD
+// walks a contiguous run of tiles. Wave-uniform result.
+struct RowTile {
+  int expert, row0, row_end, n_idx;
+  bool valid;
+};
+
+__device__ __forceinline__ RowTile find_row_tile(const int32_t *__restrict__ off, int E_L, int tm,
+                                                 int n_tiles_n) {
+  const int lane = threadIdx.x & 63;
+  RowTile tl;
+  tl.valid = false;
+  int total_m = 0;
+  for (int c = 0; c < E_L; c += 64) {
+    const int j = c + lane;
+    const int n = (j < E_L) ? off[j + 1] - off[j] : 0;
+    const int incl = wave_incl_scan((n + tm - 1) / tm);
+    total_m += __shfl(incl, 63, 64);
+  }
+  const int total = total_m * n_tiles_n;
+  const int q = (total + kNumXcd - 1) / kNumXcd;
+  const int b = blockIdx.x;
+  const int slot = b / kNumXcd;
+  const int L = (b % kNumXcd) * q + slot;
+  if (slot >= q || L >= total) return tl;
+  const int m_glob = L / n_tiles_n;
+  tl.n_idx = L - m_glob * n_tiles_n;
+  int run = 0;
+  for (int c = 0; c < E_L; c += 64) {
+    const int j = c + lane;
+    const int n = (j < E_L) ? off[j + 1] - off[j] : 0;
+    const int mt = (n + tm - 1) / tm;
+    const int incl = wave_incl_scan(mt);
+    const int tot = __shfl(incl, 63, 64);
+    if (m_glob < run + tot) {
+      const uint64_t hit = __ballot(m_glob < run + incl);
+      const int first = __builtin_ctzll(hit);
+      const int excl = __shfl(incl - mt, first, 64);
+      const int e = c + first;
+      tl.expert = e;
+      tl.row0 = off[e] + (m_glob - run - excl) * tm;
+      tl.row_end = off[e + 1];
+      tl.valid = true;
+      return tl;
+    }
+    run += tot;
+  }
+  return tl;
+}
+
 }  // namespace moe

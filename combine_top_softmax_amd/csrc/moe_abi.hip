@@ -217,4 +217,63 @@ int moe_route_bwd(const moe_shape_t *shape, const int32_t *topk_idx, const float
   return moe::launch_route_bwd(*shape, topk_idx, topk_w, dw, dlogits, stream);
 }
 
+static int check_mx_shape(const moe_shape_t *s) {
+  const int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (s->dtype != MOE_BF16) return MOE_EDTYPE;
+  if (s->d % 128 != 0 || s->F % 128 != 0) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int moe_mx_quantize_rows(int64_t rows, int32_t cols, const void *src, uint8_t *qdata,
+                         uint8_t *scales, hipStream_t stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 != 0 || rows >= ((int64_t)1 << 31)) return MOE_EINVAL;
+  if (rows == 0) return MOE_OK;
+  if (!aligned16(src) || !aligned16(qdata) || scales == nullptr) return MOE_EALIGN;
+  return moe::launch_quantize_rows(rows, cols, src, qdata, scales, stream);
+}
+
+int moe_dispatch_rows_mx(const moe_shape_t *shape, const void *x, const int32_t *dest_rank,
+                         const int32_t *dest_row, uint8_t *qbuf, uint8_t *sbuf,
+                         hipStream_t stream) {
+  const int rc = check_mx_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (shape->T == 0) return MOE_OK;
+  if (!aligned16(x) || !aligned16(qbuf) || !aligned4(sbuf) || !aligned4(dest_rank) ||
+      !aligned4(dest_row))
+    return MOE_EALIGN;
+  return moe::launch_dispatch_mx(*shape, x, dest_rank, dest_row, qbuf, sbuf, stream);
+}
+
+int moe_expert_up_mx(const moe_shape_t *shape, const uint8_t *qbuf, const uint8_t *sbuf,
+                     const int32_t *offsets, const uint8_t *w_gu_q, const uint8_t *w_gu_s,
+                     uint8_t *h_q, uint8_t *h_s, hipStream_t stream) {
+  const int rc = check_mx_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!aligned16(qbuf) || !aligned4(sbuf) || !aligned4(offsets) || !aligned16(w_gu_q) ||
+      !aligned4(w_gu_s) || !aligned16(h_q) || !aligned4(h_s))
+    return MOE_EALIGN;
+  return moe::launch_expert_up_mx(*shape, qbuf, sbuf, offsets, w_gu_q, w_gu_s, h_q, h_s, stream);
+}
+
+int moe_expert_down_mx(const moe_shape_t *shape, const uint8_t *h_q, const uint8_t *h_s,
+                       const int32_t *offsets, const uint8_t *w_d_q, const uint8_t *w_d_s,
+                       void *y, hipStream_t stream) {
+  const int rc = check_mx_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!aligned16(h_q) || !aligned4(h_s) || !aligned4(offsets) || !aligned16(w_d_q) ||
+      !aligned4(w_d_s) || !aligned16(y))
+    return MOE_EALIGN;
+  return moe::launch_expert_down_mx(*shape, h_q, h_s, offsets, w_d_q, w_d_s, y, stream);
+}
+
+int moe_expert_ffn_mx(const moe_shape_t *shape, const uint8_t *qbuf, const uint8_t *sbuf,
+                      const int32_t *offsets, const uint8_t *w_gu_q, const uint8_t *w_gu_s,
+                      const uint8_t *w_d_q, const uint8_t *w_d_s, uint8_t *h_q, uint8_t *h_s,
+                      void *y, hipStream_t stream) {
+  int rc = moe_expert_up_mx(shape, qbuf, sbuf, offsets, w_gu_q, w_gu_s, h_q, h_s, stream);
+  if (rc != MOE_OK) return rc;
+  return moe_expert_down_mx(shape, h_q, h_s, offsets, w_d_q, w_d_s, y, stream);
+}
+
 }  // extern "C"

@@ -43,6 +43,17 @@ int launch_combine_bwd(const moe_shape_t &s, const void *dout, const void *y,
                        float *dw, hipStream_t st);
 int launch_route_bwd(const moe_shape_t &s, const int32_t *idx, const float *w, const float *dw,
                      float *dlogits, hipStream_t st);
+// MXFP8 forward.
+int launch_quantize_rows(int64_t rows, int cols, const void *src, uint8_t *qdata, uint8_t *scales,
+                         hipStream_t st);
+int launch_dispatch_mx(const moe_shape_t &s, const void *x, const int32_t *dest_rank,
+                       const int32_t *dest_row, uint8_t *qbuf, uint8_t *sbuf, hipStream_t st);
+int launch_expert_up_mx(const moe_shape_t &s, const uint8_t *qbuf, const uint8_t *sbuf,
+                        const int32_t *offsets, const uint8_t *w_gu_q, const uint8_t *w_gu_s,
+                        uint8_t *h_q, uint8_t *h_s, hipStream_t st);
+int launch_expert_down_mx(const moe_shape_t &s, const uint8_t *h_q, const uint8_t *h_s,
+                          const int32_t *offsets, const uint8_t *w_d_q, const uint8_t *w_d_s,
+                          void *y, hipStream_t st);
 int launch_expert_ffn_bwd_data(const moe_shape_t &s, const void *buf, const int32_t *offsets,
                                const void *w_gu, const void *w_down, const void *dy, void *gu,
                                void *dgu, void *dx_rows, hipStream_t st);

@@ -247,6 +247,58 @@ int moe_dispatch_bwd(const moe_shape_t *shape, const void *dx_rows, const int32_
 int moe_route_bwd(const moe_shape_t *shape, const int32_t *topk_idx, const float *topk_w,
                   const float *dw, float *dlogits, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * MXFP8 forward of a bf16 layer (Olmo-core MoE report Sec. 5.5: rows are
+ * quantized during dispatch and the expert grouped GEMM consumes the
+ * quantized data and scales directly; Sec. 5.8: a route's qdata row and scale
+ * row follow the same destination indices and validity mask; Sec. 5.9: E4M3
+ * data with E8M0 scales, MXFP8 expert GEMMs, forward combine in BF16 --
+ * moe_combine on the bf16 y).
+ * Format (the OCP microscaling format the report cites): a row of n values is
+ * stored as qdata [n] uint8 E4M3 codes (OCP "E4M3FN": bias 7, max 448, no
+ * infinities) and scales [n/32] uint8 E8M0 codes (value 2^(code - 127)), one
+ * per 32 consecutive elements. A block's scale is 2^(floor(log2 amax) - 8);
+ * each element is its value over the scale rounded to the nearest E4M3 value,
+ * ties to the even code, saturating at 448, sign bit from the value's sign;
+ * an all-zero block gets scale code 0. Requirements of the MX calls
+ * (MOE_EDTYPE / MOE_EINVAL otherwise): dtype MOE_BF16, d and F multiples of
+ * 128. Alignment: bf16 sources and qdata 16 bytes, scale arrays 4 bytes.
+ * ------------------------------------------------------------------------ */
+
+/* MX-quantize `rows` rows of `cols` bf16 values (cols % 32 == 0) along the row:
+ * src [rows, cols] -> qdata [rows, cols], scales [rows, cols/32]. Used once per
+ * weight refresh for the expert weights, along their contraction dimension:
+ * W_gu as rows = E_L*2F, cols = d; W_d as rows = E_L*d, cols = F. */
+int moe_mx_quantize_rows(int64_t rows, int32_t cols, const void *src, uint8_t *qdata,
+                         uint8_t *scales, hipStream_t stream);
+
+/* Quantize-on-dispatch: token row x[t] (bf16, [T,d]) MX-quantized along d;
+ * its qdata and scale rows are written to row dest_row[t,k] of qbuf
+ * [E_L*C, d] and sbuf [E_L*C, d/32] for every route with dest_rank[t,k] ==
+ * ep_rank. Rows after the packed prefix are not written. T == 0: MOE_OK. */
+int moe_dispatch_rows_mx(const moe_shape_t *shape, const void *x, const int32_t *dest_rank,
+                         const int32_t *dest_row, uint8_t *qbuf, uint8_t *sbuf,
+                         hipStream_t stream);
+
+/* MXFP8 grouped expert FFN over the packed prefix (offsets as moe_expert_ffn):
+ * up:   H = silu(X W_gate^T) * (X W_up^T) from qbuf/sbuf and the quantized
+ *       W_gu (w_gu_q [E_L,2F,d], w_gu_s [E_L,2F,d/32]); fp32 accumulation, H
+ *       rounded to bf16 and MX-quantized along F into h_q [E_L*C, F] and
+ *       h_s [E_L*C, F/32];
+ * down: Y = H W_d^T from h_q/h_s and the quantized W_d (w_d_q [E_L,d,F],
+ *       w_d_s [E_L,d,F/32]); Y [E_L*C, d] bf16 (round to nearest even).
+ * Only prefix rows are written. */
+int moe_expert_up_mx(const moe_shape_t *shape, const uint8_t *qbuf, const uint8_t *sbuf,
+                     const int32_t *offsets, const uint8_t *w_gu_q, const uint8_t *w_gu_s,
+                     uint8_t *h_q, uint8_t *h_s, hipStream_t stream);
+int moe_expert_down_mx(const moe_shape_t *shape, const uint8_t *h_q, const uint8_t *h_s,
+                       const int32_t *offsets, const uint8_t *w_d_q, const uint8_t *w_d_s,
+                       void *y, hipStream_t stream);
+int moe_expert_ffn_mx(const moe_shape_t *shape, const uint8_t *qbuf, const uint8_t *sbuf,
+                      const int32_t *offsets, const uint8_t *w_gu_q, const uint8_t *w_gu_s,
+                      const uint8_t *w_d_q, const uint8_t *w_d_s, uint8_t *h_q, uint8_t *h_s,
+                      void *y, hipStream_t stream);
+
 /* Human-readable text of a return code (static storage, never NULL). */
 const char *moe_strerror(int code);
 

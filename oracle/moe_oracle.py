@@ -61,7 +61,8 @@ __all__ = [
     "moe_layer", "local_offsets", "combine_bwd", "expert_ffn_bwd_rows", "expert_ffn_bwd",
     "dispatch_bwd", "route_bwd", "moe_layer_bwd",
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "e8m0_decode", "mx_quantize", "mx_dequantize",
-    "dispatch_mx", "expert_ffn_mx_rows", "expert_ffn_mx", "moe_layer_mx",
+    "dispatch_mx", "expert_up_mx_rows", "expert_down_mx_rows", "expert_ffn_mx_rows",
+    "expert_ffn_mx", "moe_layer_mx",
 ]
 
 
@@ -585,22 +586,32 @@ def dispatch_mx(x, dest_rank, dest_row, ep_rank: int, n_rows: int):
     return qb, sb, written
 
 
-def expert_ffn_mx_rows(Xq, Xs, gu_q, gu_s, d_q, d_s):
-    """SwiGLU MLP of one expert on MXFP8 operands: the float64 products of the
-    dequantized operands; H = silu(G) * U rounded to bf16 and MX-quantized
-    along F for the down projection; Y rounded to bf16.
-    Xq/Xs: rows' qdata/scales along d; gu_q/gu_s: W_gu[j] [2F, d] quantized
-    along d; d_q/d_s: W_d[j] [d, F] quantized along F.
-    Returns (Hq, Hs, Y) with Y float64 holding bf16 values."""
+def expert_up_mx_rows(Xq, Xs, gu_q, gu_s):
+    """Up half of the MXFP8 expert: G, U are the float64 products of the
+    dequantized rows and W_gu[j] (gu_q/gu_s: [2F, d] quantized along d);
+    H = silu(G) * U rounded to bf16, then MX-quantized along F.
+    Returns (Hq [rows, F], Hs [rows, F/32])."""
     X = mx_dequantize(Xq, Xs)
     W = mx_dequantize(gu_q, gu_s)
     F = W.shape[0] // 2
     G = X @ W[:F].T
     U = X @ W[F:].T
-    H = round_bf16(silu(G) * U)
-    Hq, Hs = mx_quantize(H)
-    Y = round_bf16(mx_dequantize(Hq, Hs) @ mx_dequantize(d_q, d_s).T)
-    return Hq, Hs, Y
+    return mx_quantize(round_bf16(silu(G) * U))
+
+
+def expert_down_mx_rows(Hq, Hs, d_q, d_s):
+    """Down half of the MXFP8 expert: Y = dequantized H times dequantized
+    W_d[j]^T (d_q/d_s: [d, F] quantized along F), rounded to bf16.
+    Returns Y float64 [rows, d] holding bf16 values."""
+    return round_bf16(mx_dequantize(Hq, Hs) @ mx_dequantize(d_q, d_s).T)
+
+
+def expert_ffn_mx_rows(Xq, Xs, gu_q, gu_s, d_q, d_s):
+    """SwiGLU MLP of one expert on MXFP8 operands: expert_up_mx_rows, then
+    expert_down_mx_rows on the quantized H. Xq/Xs: rows' qdata/scales along d.
+    Returns (Hq, Hs, Y) with Y float64 holding bf16 values."""
+    Hq, Hs = expert_up_mx_rows(Xq, Xs, gu_q, gu_s)
+    return Hq, Hs, expert_down_mx_rows(Hq, Hs, d_q, d_s)
 
 
 def expert_ffn_mx(qbuf, sbuf, offsets_local, gu_q, gu_s, d_q, d_s):

@@ -1,0 +1,297 @@
+"""GPU parity of the MXFP8 forward (quantize-on-dispatch, MXFP8 expert GEMMs,
+BF16 combine) against the oracle's MXFP8 functions.
+
+Bars: quantized codes and scales are integers decided from exact values
+(block amax, a power-of-two scale, round to nearest even), so the row
+quantizer and quantize-on-dispatch are bit-exact. The quantized H comes out of
+fp32 GEMM accumulation and may sit on the other side of a rounding boundary
+than the float64 oracle's, so it is compared dequantized, element by element
+within one E4M3 step (or the scaled MFMA's accumulation error), with at
+least 99% of codes and scales identical. Stage tests feed both sides the same
+quantized operands (made by the oracle from seeded inputs) and hold Y to the
+BF16 path's per-row bar (2e-2); end to end, Y and the combined output inherit
+the H code flips and use a two-level bar (every row 5e-2, median row 1e-2).
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import combine_top_softmax_amd as moe
+from combine_top_softmax_amd import _abi
+from combine_top_softmax_amd.workloads import LayerConfig, CONFIGS, make_inputs, random_rows
+from oracle import moe_oracle as orc
+from gpu_util import (assert_rows_close, check_route, is_poison, oracle_route, poison_, to_np)
+
+pytestmark = pytest.mark.gpu
+
+MX_SMALL = [
+    LayerConfig("mx_small", T=1000, d=256, N=16, K=4, F=256, cf=Fraction(5, 4), dtype="bf16",
+                seed=41),
+    LayerConfig("mx_shard_ragged", T=777, d=384, N=32, K=4, F=384, cf=Fraction(1), dtype="bf16",
+                ep_size=4, ep_rank=1, seed=42),
+    LayerConfig("mx_zipf_drops", T=1500, d=128, N=24, K=3, F=128, cf=Fraction(1), dtype="bf16",
+                logits="zipf", zipf_s=1.1, seed=43),
+    LayerConfig("mx_many_experts", T=300, d=128, N=320, K=8, F=128, cf=Fraction(2),
+                dtype="bf16", ep_size=2, ep_rank=1, seed=44),
+]
+
+
+def _f64(t):
+    return t.to(torch.float64).cpu().numpy()
+
+
+def _u8(t):
+    return t.cpu().numpy()
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _wide_rows(rows, cols, seed):
+    """bf16 rows whose 32-element blocks span many magnitudes, with an
+    all-zero block, signed zeros, subnormal-range and huge values."""
+    g = torch.Generator()
+    g.manual_seed(seed)
+    v = torch.randn(rows, cols, generator=g, dtype=torch.float64)
+    v *= torch.exp2(torch.randint(-40, 40, (rows, cols // 32), generator=g).double()).repeat_interleave(32, 1)
+    v[0, :32] = 0.0
+    if rows > 1:
+        v[1, :32] = -0.0
+        v[1, 32:64] = torch.randn(32, generator=g, dtype=torch.float64) * 1e-38
+    return v.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (5, 96), (129, 2048), (64, 4096)])
+def test_quantize_rows_bit_exact(rows, cols):
+    print(f"[case] quantize rows {rows}x{cols}", flush=True)
+    src = _wide_rows(rows, cols, seed=rows * 7 + cols)
+    q = poison_(torch.empty(rows, cols, dtype=torch.uint8, device="cuda"))
+    s = poison_(torch.empty(rows, cols // 32, dtype=torch.uint8, device="cuda"))
+    moe.moe_mx_quantize_rows(src.cuda(), q, s)
+    torch.cuda.synchronize()
+    eq, es = orc.mx_quantize(_f64(src))
+    np.testing.assert_array_equal(_u8(q), eq)
+    np.testing.assert_array_equal(_u8(s), es)
+
+
+@pytest.mark.parametrize("cfg", MX_SMALL, ids=lambda c: c.name)
+def test_dispatch_mx_bit_exact(cfg):
+    print(f"[case] dispatch mx {cfg.name}", flush=True)
+    inp = make_inputs(cfg, "cpu", with_weights=False)
+    ref = oracle_route(cfg, inp.logits)
+    shape = moe.MoeShape.from_config(cfg)
+    qb = poison_(torch.empty(shape.rows, cfg.d, dtype=torch.uint8, device="cuda"))
+    sb = poison_(torch.empty(shape.rows, cfg.d // 32, dtype=torch.uint8, device="cuda"))
+    moe.moe_dispatch_rows_mx(shape, inp.x.cuda(), _dev(ref["dest_rank"]), _dev(ref["dest_row"]),
+                             qb, sb)
+    torch.cuda.synchronize()
+    eq, es, written = orc.dispatch_mx(_f64(inp.x), ref["dest_rank"], ref["dest_row"],
+                                      cfg.ep_rank, shape.rows)
+    n = int(ref["offsets"][cfg.ep_rank, -1])
+    assert written[:n].all() and not written[n:].any()
+    np.testing.assert_array_equal(_u8(qb[:n]), eq[:n])
+    np.testing.assert_array_equal(_u8(sb[:n]), es[:n])
+    assert bool(is_poison(qb[n:]).all()) and bool(is_poison(sb[n:]).all())
+
+
+# The scaled MFMA does not accumulate as exactly as fp32 FMAs: measured on the
+# device, H elements computed from the same quantized operands differ from
+# the float64 oracle (and from the bf16 GEMM on the dequantized operands,
+# which matches the oracle) by up to ~2^-16 of their block's amax. It shows
+# only on elements that nearly cancel, far below the block maximum, where the
+# E4M3 subnormal step is finer still. Bound used: 16x that.
+MFMA_MX_ABS = 2.0 ** -12
+
+
+def _check_h(hq, hs, eq, es, what):
+    """Quantized H against the oracle's: H before quantization differs by the
+    GEMM's accumulation error, so an element may round to a neighbouring E4M3
+    value and a block whose amax sits on a power of two may take the
+    neighbouring scale (its elements then sit on a grid twice as coarse).
+    Bars: block scales equal or one apart, >= 99% of codes and scales
+    identical, and every dequantized element within one E4M3 step of the
+    oracle's (the step at the larger magnitude on the coarser scale) or within
+    MFMA_MX_ABS of the block's amax."""
+    ds = hs.astype(np.int64) - es.astype(np.int64)
+    assert np.all(np.abs(ds) <= 1), f"{what}: a block scale differs by more than one"
+    assert np.mean(hq == eq) >= 0.99, f"{what}: codes agree on {np.mean(hq == eq):.4f}"
+    assert np.mean(hs == es) >= 0.99, f"{what}: scales agree on {np.mean(hs == es):.4f}"
+    g, o = orc.mx_dequantize(hq, hs), orc.mx_dequantize(eq, es)
+    Xc = np.repeat(np.maximum(orc.e8m0_decode(hs), orc.e8m0_decode(es)), 32, axis=1)
+    a = np.maximum(np.abs(g), np.abs(o)) / Xc
+    step = np.where(a >= 2.0 ** -6, np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3),
+                    2.0 ** -9) * Xc
+    amax = np.maximum(np.abs(g).reshape(len(g), -1, 32).max(axis=2),
+                      np.abs(o).reshape(len(o), -1, 32).max(axis=2))
+    bound = np.maximum(step, MFMA_MX_ABS * np.repeat(amax, 32, axis=1))
+    bad = np.abs(g - o) > bound * (1 + 1e-12)
+    assert not bad.any(), f"{what}: {bad.sum()} elements past the bound"
+
+
+@pytest.mark.parametrize("cfg", MX_SMALL, ids=lambda c: c.name)
+def test_expert_up_down_mx_stages(cfg):
+    """Each GEMM on the oracle's own quantized operands."""
+    print(f"[case] expert mx stages {cfg.name}", flush=True)
+    inp = make_inputs(cfg, "cpu")
+    ref = oracle_route(cfg, inp.logits)
+    shape = moe.MoeShape.from_config(cfg)
+    E_L, d, F = cfg.E_L, cfg.d, cfg.F
+    qb, sb, _ = orc.dispatch_mx(_f64(inp.x), ref["dest_rank"], ref["dest_row"], cfg.ep_rank,
+                                shape.rows)
+    gq, gs = orc.mx_quantize(_f64(inp.w_gu).reshape(-1, d))
+    dq, ds = orc.mx_quantize(_f64(inp.w_d).reshape(-1, F))
+    gq, gs = gq.reshape(E_L, 2 * F, d), gs.reshape(E_L, 2 * F, d // 32)
+    dq, ds = dq.reshape(E_L, d, F), ds.reshape(E_L, d, F // 32)
+    off = ref["offsets"][cfg.ep_rank]
+    n = int(off[-1])
+    hq = poison_(torch.empty(shape.rows, F, dtype=torch.uint8, device="cuda"))
+    hs = poison_(torch.empty(shape.rows, F // 32, dtype=torch.uint8, device="cuda"))
+    moe.moe_expert_up_mx(shape, _dev(qb), _dev(sb), _dev(ref["offsets"]), _dev(gq), _dev(gs),
+                         hq, hs)
+    # the down GEMM gets the oracle's H, so each stage is judged on its own
+    eHq = np.zeros((shape.rows, F), np.uint8)
+    eHs = np.zeros((shape.rows, F // 32), np.uint8)
+    eY = np.full((shape.rows, d), np.nan)
+    for j in range(E_L):
+        a, b = int(off[j]), int(off[j + 1])
+        if b > a:
+            eHq[a:b], eHs[a:b] = orc.expert_up_mx_rows(qb[a:b], sb[a:b], gq[j], gs[j])
+            eY[a:b] = orc.expert_down_mx_rows(eHq[a:b], eHs[a:b], dq[j], ds[j])
+    y = poison_(torch.empty(shape.rows, d, dtype=torch.bfloat16, device="cuda"))
+    moe.moe_expert_down_mx(shape, _dev(eHq), _dev(eHs), _dev(ref["offsets"]), _dev(dq), _dev(ds),
+                           y)
+    torch.cuda.synchronize()
+    if n > 0:
+        _check_h(_u8(hq[:n]), _u8(hs[:n]), eHq[:n], eHs[:n], "h")
+        assert_rows_close(to_np(y[:n]), eY[:n], 2e-2, "y")
+    assert bool(is_poison(hq[n:]).all()) and bool(is_poison(hs[n:]).all())
+    assert bool(is_poison(y[n:]).all())
+
+
+# End to end, the GPU's H is its own: its codes sit on the other side of a
+# rounding boundary from the oracle's for a fraction of a percent of the
+# elements (each such flip moves an element by up to one E4M3 step, 12.5% of
+# it), and Y and the output inherit that. Each GEMM is held to the BF16 bar on
+# identical operands above; end to end the bar is two-level: every row within
+# 5e-2 and the median row within 1e-2 (a scale or layout mistake moves the
+# median by orders of magnitude, isolated flips move single rows).
+E2E_ROW, E2E_MEDIAN = 5e-2, 1e-2
+MX_LAYER = MX_SMALL[:2] + [MX_SMALL[2].with_(name="mx_zipf_drops_256", d=256, F=256),
+                           MX_SMALL[3].with_(name="mx_many_experts_256", d=256, F=256)]
+
+
+def _check_e2e(got, ref, what):
+    worst = assert_rows_close(got, ref, E2E_ROW, what)
+    nz = ~np.all(ref == 0, axis=1)
+    err = np.linalg.norm(got[nz] - ref[nz], axis=1) / np.linalg.norm(ref[nz], axis=1)
+    assert np.median(err) <= E2E_MEDIAN, f"{what}: median row error {np.median(err):.3e}"
+    return worst
+
+
+@pytest.mark.parametrize("cfg", MX_LAYER, ids=lambda c: c.name)
+def test_layer_mx_matches_oracle(cfg):
+    """MoELayer.forward_mx (weights quantized on the GPU) against moe_layer_mx."""
+    print(f"[case] layer mx {cfg.name}", flush=True)
+    inp = make_inputs(cfg, "cpu")
+    shape = moe.MoeShape.from_config(cfg)
+    layer = moe.MoELayer(shape, "cuda")
+    layer.alloc_mx("cuda")
+    for t in (layer.qbuf, layer.sbuf, layer.h_q, layer.h_s, layer.y, layer.out):
+        poison_(t)
+    mxw = moe.MxWeights.from_bf16(inp.w_gu.cuda(), inp.w_d.cuda())
+    layer.forward_mx(inp.logits.cuda(), inp.x.cuda(), mxw)
+    torch.cuda.synchronize()
+    ref = orc.moe_layer_mx(inp.logits.numpy(), _f64(inp.x), _f64(inp.w_gu), _f64(inp.w_d),
+                           cfg.K, cfg.capacity, cfg.ep_size, cfg.ep_rank)
+    check_route(layer.route, ref, shape)
+    np.testing.assert_array_equal(_u8(mxw.w_gu_q), ref["w_gu_q"])
+    np.testing.assert_array_equal(_u8(mxw.w_gu_s), ref["w_gu_s"])
+    np.testing.assert_array_equal(_u8(mxw.w_d_q), ref["w_d_q"])
+    np.testing.assert_array_equal(_u8(mxw.w_d_s), ref["w_d_s"])
+    n = int(ref["offsets"][cfg.ep_rank, -1])
+    np.testing.assert_array_equal(_u8(layer.qbuf[:n]), ref["qbuf"][:n])
+    np.testing.assert_array_equal(_u8(layer.sbuf[:n]), ref["sbuf"][:n])
+    if n > 0:
+        _check_h(_u8(layer.h_q[:n]), _u8(layer.h_s[:n]), ref["h_q"][:n], ref["h_s"][:n], "h")
+        _check_e2e(to_np(layer.y[:n]), ref["y"][:n], "y")
+    assert bool(is_poison(layer.y[n:]).all())
+    _check_e2e(to_np(layer.out), ref["out"], "out")
+
+
+@pytest.mark.parametrize("name", ["olmoe_bf16", "zipf_skew_bf16", "finegrained_shard_bf16"])
+def test_full_config_mx(name):
+    """Full workload sizes: MoELayer.forward_mx; routing and quantize-on-dispatch
+    checked on sampled rows bit-exactly, the expert outputs of sampled rows of
+    sampled experts and the combined output of sampled tokens recomputed one
+    by one by the oracle."""
+    cfg = CONFIGS[name]
+    print(f"[case] full mx {name}", flush=True)
+    inp = make_inputs(cfg, "cuda")
+    shape = moe.MoeShape.from_config(cfg)
+    layer = moe.MoELayer(shape, "cuda")
+    mxw = moe.MxWeights.from_bf16(inp.w_gu, inp.w_d)
+    layer.forward_mx(inp.logits, inp.x, mxw)
+    torch.cuda.synchronize()
+    ref = oracle_route(cfg, inp.logits.cpu())
+    check_route(layer.route, ref, shape)
+    rng = np.random.default_rng(cfg.seed + 5)
+    K, E_L, d, F = cfg.K, cfg.E_L, cfg.d, cfg.F
+    off = ref["offsets"][cfg.ep_rank]
+    n = int(off[-1])
+    x = _f64(inp.x)
+    # quantize-on-dispatch on sampled rows
+    rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 256)]))
+    src = ref["row_src"][rows] // K
+    eq, es = orc.mx_quantize(x[src])
+    sel = torch.from_numpy(rows).cuda()
+    np.testing.assert_array_equal(_u8(layer.qbuf[sel]), eq)
+    np.testing.assert_array_equal(_u8(layer.sbuf[sel]), es)
+    # expert outputs on sampled rows of sampled experts (the GPU's quantized
+    # weights of those experts checked bit-exactly first, then used by the oracle)
+    nonempty = [j for j in range(E_L) if off[j + 1] > off[j]]
+    experts = sorted({nonempty[0], nonempty[-1], int(rng.choice(nonempty))})
+    wcache = {}
+
+    def wq(j):
+        if j not in wcache:
+            gq, gs = orc.mx_quantize(_f64(inp.w_gu[j]))
+            dq, ds = orc.mx_quantize(_f64(inp.w_d[j]))
+            wcache[j] = (gq, gs, dq, ds)
+        return wcache[j]
+
+    for j in experts:
+        gq, gs, dq, ds = wq(j)
+        np.testing.assert_array_equal(_u8(mxw.w_gu_q[j]), gq)
+        np.testing.assert_array_equal(_u8(mxw.w_d_s[j]), ds)
+        a, b = int(off[j]), int(off[j + 1])
+        rr = np.unique(np.concatenate([[a, b - 1], rng.integers(a, b, 12)]))
+        Xq, Xs = orc.mx_quantize(x[ref["row_src"][rr] // K])
+        Hq, Hs, Y = orc.expert_ffn_mx_rows(Xq, Xs, gq, gs, dq, ds)
+        s2 = torch.from_numpy(rr).cuda()
+        _check_h(_u8(layer.h_q[s2]), _u8(layer.h_s[s2]), Hq, Hs, f"h expert {j}")
+        assert_rows_close(to_np(layer.y[s2]), Y, E2E_ROW, f"y expert {j}")
+    # combined output on sampled tokens
+    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 6)]))
+
+    def y_of_row(row):
+        j = int(np.searchsorted(off, row, side="right") - 1)
+        gq, gs, dq, ds = wq(j)
+        Xq, Xs = orc.mx_quantize(x[int(ref["row_src"][row] // K)][None])
+        return orc.expert_ffn_mx_rows(Xq, Xs, gq, gs, dq, ds)[2][0]
+
+    expect = orc.combine_tokens(toks, y_of_row, ref["dest_rank"], ref["dest_row"], ref["topk_w"],
+                                cfg.ep_rank, d, "bf16")
+    assert_rows_close(to_np(layer.out[torch.from_numpy(toks).cuda()]), expect, E2E_ROW, "out")
+
+
+def test_mx_calls_reject_what_they_do_not_cover():
+    lib = _abi.load()
+    import ctypes
+    f32 = moe.MoeShape.from_config(MX_SMALL[0].with_(dtype="f32")).c()
+    assert lib.moe_dispatch_rows_mx(ctypes.byref(f32), 16, 16, 16, 16, 16, None) == _abi.MOE_EDTYPE
+    odd = moe.MoeShape.from_config(CONFIGS["gptoss_shard_bf16"]).c()   # d = 2880
+    assert lib.moe_expert_up_mx(ctypes.byref(odd), *([16] * 7), None) == _abi.MOE_EINVAL
+    assert lib.moe_mx_quantize_rows(4, 48, 16, 16, 16, None) == _abi.MOE_EINVAL
