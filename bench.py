@@ -38,6 +38,8 @@ def parse():
                    help="target CPU time of the oracle sample")
     p.add_argument("--no-backward", action="store_true",
                    help="skip the timing of the layer backward (reported beside the forward)")
+    p.add_argument("--no-mx", action="store_true",
+                   help="skip the timing of the MXFP8 forward (reported beside the BF16 one)")
     p.add_argument("--traffic-probe", action="store_true",
                    help="run 3 layer forwards, then 3 plain 512 MiB device copies (the "
                         "calibration kernel for rocprofv3 FETCH_SIZE / WRITE_SIZE), and exit")
@@ -96,6 +98,62 @@ def cpu_baseline(cfg, target_s: float) -> dict:
                       f"the {cfg.name} shape, same input recipe, capacity recomputed for {T_s} "
                       f"tokens: {rows} routed rows in {dt:.2f} s; NumPy float64, "
                       f"BLAS threads={threads}"}
+
+
+MX_STAGES = ["route", "dispatch_mx", "up_mx", "down_mx", "combine"]
+MFMA_FP8_PEAK_TFLOPS = 5033.2   # dense fp8 / MX-fp8 MFMA (2x the bf16 rate)
+
+
+def time_mx(args, layer, inp, stream, torch) -> dict:
+    """MXFP8 forward of the same layer (quantize-on-dispatch, MXFP8 expert
+    GEMMs, BF16 combine), timed like the BF16 step. The expert weights are
+    quantized once before the loop (a weight-refresh cost, not per step).
+    Not part of ``value``."""
+    import combine_top_softmax_amd as moe
+    s = layer.shape
+    if s.dtype != "bf16" or s.d % 128 or s.F % 128:
+        return {"skipped": "the MXFP8 path needs a bf16 layer with d and F multiples of 128"}
+    mxw = moe.MxWeights.from_bf16(inp.w_gu, inp.w_d)
+    layer.alloc_mx("cuda")
+
+    def mstep(ev=None):
+        if ev: ev[0].record(stream)
+        layer.route_step(inp.logits)
+        if ev: ev[1].record(stream)
+        layer.dispatch_mx_step(inp.x)
+        if ev: ev[2].record(stream)
+        layer.up_mx_step(mxw)
+        if ev: ev[3].record(stream)
+        layer.down_mx_step(mxw)
+        if ev: ev[4].record(stream)
+        layer.combine_step()
+        if ev: ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        mstep()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.set_sync_debug_mode("error")
+    for i in range(args.steps):
+        mstep(evs[i])
+    torch.cuda.set_sync_debug_mode(0)
+    torch.cuda.synchronize()
+    ms = evs[0][0].elapsed_time(evs[-1][5]) / args.steps
+    st = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+          for i, n in enumerate(MX_STAGES)}
+    R = int(layer.route.offsets[s.ep_rank, -1].item())
+    S = int((layer.route.dest_rank == s.ep_rank).any(dim=1).sum().item())
+    rdf = float(R) * s.d * s.F
+    t_up, t_dn = st["up_mx"] * 1e-3, st["down_mx"] * 1e-3
+    disp_bytes = S * s.d * 2 + R * (s.d + s.d // 32) + 8 * s.T * s.K
+    return {"ms_per_step": round(ms, 5),
+            "routed_rows_per_s": round(R / (ms * 1e-3), 1),
+            "stages_ms": {n: round(v, 5) for n, v in st.items()},
+            "up_TFLOPs": round(4 * rdf / t_up / 1e12, 1),
+            "down_TFLOPs": round(2 * rdf / t_dn / 1e12, 1),
+            "gemm_TFLOPs": round(6 * rdf / (t_up + t_dn) / 1e12, 1),
+            "gemm_mfma_fp8_frac": round(6 * rdf / (t_up + t_dn) / 1e12 / MFMA_FP8_PEAK_TFLOPS, 4),
+            "dispatch_mx_GBps": round(disp_bytes / (st["dispatch_mx"] * 1e-3) / 1e9, 1)}
 
 
 BWD_STAGES = ["combine_bwd", "expert_ffn_bwd_data", "dispatch_bwd", "route_bwd",
@@ -225,6 +283,7 @@ def main():
     graph_ms = g0.elapsed_time(g1) / args.steps
 
     backward = None if args.no_backward else time_backward(args, layer, inp, stream, torch)
+    mx = None if args.no_mx else time_mx(args, layer, inp, stream, torch)
 
     total_ms = evs[0][0].elapsed_time(evs[-1][5])
     ms_step = total_ms / args.steps
@@ -300,6 +359,7 @@ def main():
         "host_enqueue_ms_per_step": round(t_host * 1e3 / args.steps, 4),
         "graph_replay_ms_per_step": round(graph_ms, 5),
         "backward": backward,
+        "mxfp8_forward": mx,
         "stages": stages,
         "roofline": roof,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_seconds),
