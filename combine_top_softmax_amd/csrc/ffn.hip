@@ -33,6 +33,8 @@
 //   k_gemm_bf16 (any K % 8 == 0): 128 x 128 block tile, 4 waves of 64 x 64,
 //     register-staged LDS double buffer with 16-byte row padding.
 // fp32 path: a plain LDS-tiled SIMT kernel (64 x 64 tile, 4 x 4 per thread).
+#include <type_traits>
+
 #include "moe_internal.h"
 #include "gemm_common.h"
 
@@ -307,23 +309,32 @@ __device__ __forceinline__ void big_issue(const uint16_t *__restrict__ A,
 //   * fragments double-buffered across the K sub-steps: each read of
 //     sub-step ks+1 follows one MFMA of sub-step ks, so it lands while the
 //     remaining MFMAs of ks execute.
-template <bool GATE_UP, int BM, int BK, int NS, int NW>
+//
+// VT < TM (the last m-tile of an expert): only this wave's first VT 32-row
+// MFMA tiles hold valid rows; the MFMAs and A fragment reads of the others are
+// dropped at compile time, and the A direct loads in a_skip (bit d: load d
+// feeds only rows past the last valid 32-row group) are not issued. Full
+// tiles take VT = TM.
+template <bool GATE_UP, int BM, int BK, int NS, int NW, int VT = BigTile<BM, BK, NS, NW>::TM>
 __device__ __forceinline__ void big_step(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ Wj, const uint32_t *a_off,
     const uint32_t *b_off, int k0, bool do_load, int wv, uint8_t *__restrict__ ld,
     const uint8_t *__restrict__ rd, const int *fa, const int *fb, int khalf, int sw,
-    f32x16_t (&acc)[BigTile<BM, BK, NS, NW>::TM][BigTile<BM, BK, NS, NW>::TN]) {
+    f32x16_t (&acc)[BigTile<BM, BK, NS, NW>::TM][BigTile<BM, BK, NS, NW>::TN],
+    uint32_t a_skip = 0) {
   using P = BigTile<BM, BK, NS, NW>;
+  constexpr bool PARTIAL = VT < P::TM;
   constexpr int MF = P::KS * P::TM * P::TN;      // MFMAs per step
   // MFMAs between two direct loads: spread over the step, or over its first
   // half with two stages (those loads must land before the next step)
   constexpr int GAP = (NS == 2 && MF >= 2 * P::L) ? MF / (2 * P::L) : MF / P::L;
   static_assert(GAP >= 1 && GAP * P::L <= MF, "load spacing");
   auto issue_one = [&](int d) {
-    if (d < P::NA)
-      __builtin_amdgcn_global_load_lds(A + a_off[d] + k0,
-                                       MOE_LDS(ld + (wv * P::NA + d) * 1024), 16, 0, 0);
-    else
+    if (d < P::NA) {
+      if (!PARTIAL || !((a_skip >> d) & 1))
+        __builtin_amdgcn_global_load_lds(A + a_off[d] + k0,
+                                         MOE_LDS(ld + (wv * P::NA + d) * 1024), 16, 0, 0);
+    } else
       __builtin_amdgcn_global_load_lds(
           Wj + b_off[d - P::NA] + k0,
           MOE_LDS(ld + P::A_BYTES + (wv * P::NB + (d - P::NA)) * 1024), 16, 0, 0);
@@ -331,9 +342,10 @@ __device__ __forceinline__ void big_step(
   bf16x8_t fra[2][P::TM], frb[2][P::TN];
   auto read_frag = [&](int buf, int ks, int q) {
     const int cb = ((ks * 2 + khalf) ^ sw) << 4;
-    if (q < P::TM)
-      fra[buf][q] = *reinterpret_cast<const bf16x8_t *>(rd + fa[q] + cb);
-    else
+    if (q < P::TM) {
+      if (q < VT)
+        fra[buf][q] = *reinterpret_cast<const bf16x8_t *>(rd + fa[q] + cb);
+    } else
       frb[buf][q - P::TM] = *reinterpret_cast<const bf16x8_t *>(rd + fb[q - P::TM] + cb);
   };
 #pragma unroll
@@ -346,8 +358,9 @@ __device__ __forceinline__ void big_step(
     for (int q = 0; q < P::TM * P::TN; ++q) {
       const int g = ks * P::TM * P::TN + q;
       const int i = q / P::TN, j = q % P::TN;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fra[cur][i], frb[cur][j], acc[i][j],
-                                                          0, 0, 0);
+      if (i < VT)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fra[cur][i], frb[cur][j], acc[i][j],
+                                                            0, 0, 0);
       if (ks + 1 < P::KS && q < P::TM + P::TN) read_frag(cur ^ 1, ks + 1, q);
       if (do_load && g % GAP == 0 && g / GAP < P::L) issue_one(g / GAP);
       __builtin_amdgcn_sched_barrier(0);
@@ -423,24 +436,47 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int nk = Kdim / BK;
+  // valid 32-row MFMA tiles of this wave, and the A loads that feed only rows
+  // past the last valid 32-row group of the tile (wave-uniform)
+  const int nvalid = min(BM, tl.row_end - tl.row0);
+  const int vt = __builtin_amdgcn_readfirstlane(min(P::TM, max(0, (nvalid - wm * 128 + 31) / 32)));
+  uint32_t a_skip = 0;
+#pragma unroll
+  for (int i = 0; i < P::NA; ++i)
+    if ((wv * P::NA + i) * P::RPI >= ((nvalid + 31) / 32) * 32) a_skip |= 1u << i;
+  a_skip = __builtin_amdgcn_readfirstlane(a_skip);
   // prologue: K steps 0 .. NS-2 into stages 0 .. NS-2
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk)
       big_issue<BM, BK, NS, NW>(A, Wj, a_off, b_off, s * BK, wv, smem + s * P::STAGE_BYTES);
-  for (int kb = 0; kb < nk; ++kb) {
-    // this wave's loads of step kb have landed once at most the loads of
-    // steps kb+1 .. kb+NS-2 are still in flight; then every wave's have
-    if (kb + NS - 2 <= nk - 1) wait_vmcnt<(NS - 2) * P::L>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    const int ls = (kb + NS - 1) % NS;   // stage read in step kb-1: free after the barrier
-    uint8_t *ld = smem + ls * P::STAGE_BYTES;
-    const uint8_t *rd = smem + (kb % NS) * P::STAGE_BYTES;
-    big_step<GATE_UP, BM, BK, NS, NW>(A, Wj, a_off, b_off, (kb + NS - 1) * BK, kb + NS - 1 < nk, wv,
-                                  ld, rd, fa, fb, khalf, sw, acc);
+  // one main loop per count of valid 32-row tiles of this wave (TM for full
+  // tiles; fewer on an expert's last m-tile), each with a single inlined step
+  auto main_loop = [&](auto vt_tag) {
+    constexpr int VT = decltype(vt_tag)::value;
+    for (int kb = 0; kb < nk; ++kb) {
+      // this wave's loads of step kb have landed once at most the loads of
+      // steps kb+1 .. kb+NS-2 are still in flight; then every wave's have
+      if (kb + NS - 2 <= nk - 1) wait_vmcnt<(NS - 2) * P::L>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      const int ls = (kb + NS - 1) % NS;   // stage read in step kb-1: free after the barrier
+      uint8_t *ld = smem + ls * P::STAGE_BYTES;
+      const uint8_t *rd = smem + (kb % NS) * P::STAGE_BYTES;
+      big_step<GATE_UP, BM, BK, NS, NW, VT>(A, Wj, a_off, b_off, (kb + NS - 1) * BK,
+                                            kb + NS - 1 < nk, wv, ld, rd, fa, fb, khalf, sw, acc,
+                                            a_skip);
+    }
+  };
+  static_assert(P::TM == 4, "main-loop variants");
+  switch (vt) {
+    case 4: main_loop(std::integral_constant<int, 4>{}); break;
+    case 3: main_loop(std::integral_constant<int, 3>{}); break;
+    case 2: main_loop(std::integral_constant<int, 2>{}); break;
+    case 1: main_loop(std::integral_constant<int, 1>{}); break;
+    default: main_loop(std::integral_constant<int, 0>{}); break;
   }
 
   // Epilogue, staged through LDS so that global stores are whole 16-byte
