@@ -30,6 +30,8 @@
 //                  every MFMA operand is read K-contiguous.
 // G, U are recomputed by the forward NT GEMM (no activation, 2F columns);
 // dispatch backward is the forward combine kernel with unit weights.
+#include <type_traits>
+
 #include "moe_internal.h"
 #include "gemm_common.h"
 
@@ -379,6 +381,7 @@ struct BigCtx {
   int krow[bt::LPW];         // MN-contiguous tiles: k-row of each load within the step
   int fa[bt::TM], fb[bt::TN];
   int sw;
+  uint32_t a_skip;           // K-contiguous A loads that feed only rows past the valid ones
 };
 
 __device__ __forceinline__ bf16x8_t tr_pair(const uint8_t *p) {
@@ -411,8 +414,9 @@ __device__ __forceinline__ void big_issue(const BigCtx &c, int k0, int wv,
                                           uint8_t *__restrict__ stage) {
 #pragma unroll
   for (int i = 0; i < bt::LPW; ++i)
-    __builtin_amdgcn_global_load_lds(big_a_src<MODE>(c, i, k0),
-                                     MOE_LDS(stage + (wv * bt::LPW + i) * 1024), 16, 0, 0);
+    if (!((c.a_skip >> i) & 1))
+      __builtin_amdgcn_global_load_lds(big_a_src<MODE>(c, i, k0),
+                                       MOE_LDS(stage + (wv * bt::LPW + i) * 1024), 16, 0, 0);
 #pragma unroll
   for (int i = 0; i < bt::LPW; ++i)
     __builtin_amdgcn_global_load_lds(big_b_src<MODE>(c, i, k0),
@@ -422,8 +426,10 @@ __device__ __forceinline__ void big_issue(const BigCtx &c, int k0, int wv,
 
 // One main-loop step (see the forward's big_step): MFMAs of this step from
 // `rd`, one direct load of the next step into `ld` every other MFMA over the
-// first half, fragments double-buffered across the K sub-steps.
-template <int MODE>
+// first half, fragments double-buffered across the K sub-steps. VT: this
+// wave's 32-row MFMA tiles that hold valid rows (fewer than TM on a ragged
+// last tile: the others' MFMAs and A fragment reads are dropped).
+template <int MODE, int VT>
 __device__ __forceinline__ void big_step(const BigCtx &c, int k0, bool do_load, int wv,
                                          uint8_t *__restrict__ ld, const uint8_t *__restrict__ rd,
                                          int khalf, f32x16_t (&acc)[bt::TM][bt::TN]) {
@@ -431,10 +437,11 @@ __device__ __forceinline__ void big_step(const BigCtx &c, int k0, bool do_load, 
   constexpr int L = 2 * bt::LPW;                 // 8 direct loads per step
   constexpr int GAP = MF / (2 * L);
   auto issue_one = [&](int d) {
-    if (d < bt::LPW)
-      __builtin_amdgcn_global_load_lds(big_a_src<MODE>(c, d, k0),
-                                       MOE_LDS(ld + (wv * bt::LPW + d) * 1024), 16, 0, 0);
-    else
+    if (d < bt::LPW) {
+      if (VT == bt::TM || !((c.a_skip >> d) & 1))
+        __builtin_amdgcn_global_load_lds(big_a_src<MODE>(c, d, k0),
+                                         MOE_LDS(ld + (wv * bt::LPW + d) * 1024), 16, 0, 0);
+    } else
       __builtin_amdgcn_global_load_lds(big_b_src<MODE>(c, d - bt::LPW, k0),
                                        MOE_LDS(ld + bt::TILE + (wv * bt::LPW + d - bt::LPW) * 1024),
                                        16, 0, 0);
@@ -442,6 +449,7 @@ __device__ __forceinline__ void big_step(const BigCtx &c, int k0, bool do_load, 
   bf16x8_t fra[2][bt::TM], frb[2][bt::TN];
   auto read_frag = [&](int buf, int ks, int q) {
     if (q < bt::TM) {
+      if (q >= VT) return;
       if constexpr (MODE == BW_WG)
         fra[buf][q] = tr_pair(rd + c.fa[q] + ks * 16 * bt::MNROW);
       else
@@ -461,8 +469,9 @@ __device__ __forceinline__ void big_step(const BigCtx &c, int k0, bool do_load, 
     for (int q = 0; q < bt::TM * bt::TN; ++q) {
       const int g = ks * bt::TM * bt::TN + q;
       const int i = q / bt::TN, j = q % bt::TN;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fra[cur][i], frb[cur][j], acc[i][j],
-                                                          0, 0, 0);
+      if (i < VT)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fra[cur][i], frb[cur][j], acc[i][j],
+                                                            0, 0, 0);
       if (ks + 1 < bt::KS && q < bt::TM + bt::TN) read_frag(cur ^ 1, ks + 1, q);
       if (do_load && g % GAP == 0 && g / GAP < L) issue_one(g / GAP);
       __builtin_amdgcn_sched_barrier(0);
@@ -536,22 +545,44 @@ __global__ __launch_bounds__(bt::NT, 1) void k_gemm_bwd_big(GemmArgs p) {
   const int klen = wk.kend - wk.kbeg;
   const int nk = (klen + bt::BK - 1) / bt::BK;
   const int rem = klen % bt::BK;
+  // valid output rows of the tile, this wave's valid 32-row MFMA tiles, and
+  // the K-contiguous A loads that feed only rows past them (wave-uniform)
+  const int nvalid = MODE == BW_WG ? min(bt::BM, p.M - wk.m0) : min(bt::BM, wk.m_end - wk.m0);
+  const int vt = __builtin_amdgcn_readfirstlane(min(bt::TM, max(0, (nvalid - wm * 128 + 31) / 32)));
+  c.a_skip = 0;
+  if (MODE != BW_WG) {
+#pragma unroll
+    for (int i = 0; i < bt::LPW; ++i)
+      if ((wv * bt::LPW + i) * 8 >= ((nvalid + 31) / 32) * 32) c.a_skip |= 1u << i;
+  }
+  c.a_skip = __builtin_amdgcn_readfirstlane(c.a_skip);
   if (nk > 0) big_issue<MODE>(c, 0, wv, smem);
-  for (int kb = 0; kb < nk; ++kb) {
-    wait_vmcnt<0>();            // this wave's loads of step kb have landed ...
-    __builtin_amdgcn_s_barrier();   // ... and so have every wave's
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    uint8_t *ld = smem + ((kb + 1) & 1) * bt::STAGE;   // read in step kb-1: free now
-    uint8_t *rd = smem + (kb & 1) * bt::STAGE;
-    if (MODE == BW_WG && kb == nk - 1 && rem != 0) {
-      // rows past the expert's range contribute nothing: zero them in B
-      const u32x4_t z = {0, 0, 0, 0};
-      for (int o = rem * bt::MNROW + tid * 16; o < bt::TILE; o += bt::NT * 16)
-        *reinterpret_cast<u32x4_t *>(rd + bt::TILE + o) = z;
-      __syncthreads();
+  // one main loop per count of valid 32-row tiles of this wave
+  auto main_loop = [&](auto vt_tag) {
+    constexpr int VT = decltype(vt_tag)::value;
+    for (int kb = 0; kb < nk; ++kb) {
+      wait_vmcnt<0>();            // this wave's loads of step kb have landed ...
+      __builtin_amdgcn_s_barrier();   // ... and so have every wave's
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      uint8_t *ld = smem + ((kb + 1) & 1) * bt::STAGE;   // read in step kb-1: free now
+      uint8_t *rd = smem + (kb & 1) * bt::STAGE;
+      if (MODE == BW_WG && kb == nk - 1 && rem != 0) {
+        // rows past the expert's range contribute nothing: zero them in B
+        const u32x4_t z = {0, 0, 0, 0};
+        for (int o = rem * bt::MNROW + tid * 16; o < bt::TILE; o += bt::NT * 16)
+          *reinterpret_cast<u32x4_t *>(rd + bt::TILE + o) = z;
+        __syncthreads();
+      }
+      big_step<MODE, VT>(c, (kb + 1) * bt::BK, kb + 1 < nk, wv, ld, rd, khalf, acc);
     }
-    big_step<MODE>(c, (kb + 1) * bt::BK, kb + 1 < nk, wv, ld, rd, khalf, acc);
+  };
+  switch (vt) {
+    case 4: main_loop(std::integral_constant<int, 4>{}); break;
+    case 3: main_loop(std::integral_constant<int, 3>{}); break;
+    case 2: main_loop(std::integral_constant<int, 2>{}); break;
+    case 1: main_loop(std::integral_constant<int, 1>{}); break;
+    default: main_loop(std::integral_constant<int, 0>{}); break;
   }
 
   // ---- epilogues. MFMA result layout: register r of lane l holds row

@@ -34,6 +34,8 @@
 // block and bytes 16..31 from its second (any order inside a block, the same
 // for A and B); lane l's scale operand is the E8M0 code of block l / 32 of that
 // row. Here lane l takes 16-byte chunks g and 2 + g (g = l / 32) of the slice.
+#include <type_traits>
+
 #include "moe_internal.h"
 #include "gemm_common.h"
 
@@ -158,6 +160,7 @@ struct MxCtx {
   int fa[mxg::TM], fb[mxg::TN];
   int sa_lds[mxg::TM], sb_lds[mxg::TN];
   int sw;
+  uint32_t a_skip;            // A loads that feed only rows past the valid ones
 };
 
 __device__ __forceinline__ void mx_issue(const MxCtx &c, int k0, int wv,
@@ -166,8 +169,9 @@ __device__ __forceinline__ void mx_issue(const MxCtx &c, int k0, int wv,
                                    4, 0, 0);
 #pragma unroll
   for (int i = 0; i < mxg::NA; ++i)
-    __builtin_amdgcn_global_load_lds(c.A + (uint32_t)(c.a_off[i] + k0),
-                                     MOE_LDS(stage + (wv * mxg::NA + i) * 1024), 16, 0, 0);
+    if (!((c.a_skip >> i) & 1))
+      __builtin_amdgcn_global_load_lds(c.A + (uint32_t)(c.a_off[i] + k0),
+                                       MOE_LDS(stage + (wv * mxg::NA + i) * 1024), 16, 0, 0);
 #pragma unroll
   for (int i = 0; i < mxg::NB; ++i)
     __builtin_amdgcn_global_load_lds(c.W + (uint32_t)(c.b_off[i] + k0),
@@ -182,6 +186,9 @@ __device__ __forceinline__ void mx_issue(const MxCtx &c, int k0, int wv,
 // its last MFMA of this one (6 MFMAs before it is needed again), which keeps
 // the fragments at 64 VGPRs. sa/sb: this step's scale dwords (the 4 blocks of
 // the row of the lane's fragment).
+// VT: this wave's 32-row MFMA tiles that hold valid rows (fewer than TM on an
+// expert's last m-tile: the others' MFMAs and A fragment reads are dropped).
+template <int VT>
 __device__ __forceinline__ void mx_step(const MxCtx &c, int k0, int wv,
                                         uint8_t *__restrict__ ld, const uint8_t *__restrict__ rd,
                                         int g, f32x16_t (&acc)[mxg::TM][mxg::TN]) {
@@ -191,10 +198,11 @@ __device__ __forceinline__ void mx_step(const MxCtx &c, int k0, int wv,
   // k0: the K offset (bytes) of the step loaded into `ld` (the caller repeats
   // the last step on the last iteration: no branch inside the step)
   auto issue_one = [&](int d) {
-    if (d < mxg::NA)
-      __builtin_amdgcn_global_load_lds(c.A + (uint32_t)(c.a_off[d] + k0),
-                                       MOE_LDS(ld + (wv * mxg::NA + d) * 1024), 16, 0, 0);
-    else if (d < mxg::L)
+    if (d < mxg::NA) {
+      if (VT == mxg::TM || !((c.a_skip >> d) & 1))
+        __builtin_amdgcn_global_load_lds(c.A + (uint32_t)(c.a_off[d] + k0),
+                                         MOE_LDS(ld + (wv * mxg::NA + d) * 1024), 16, 0, 0);
+    } else if (d < mxg::L)
       __builtin_amdgcn_global_load_lds(
           c.W + (uint32_t)(c.b_off[d - mxg::NA] + k0),
           MOE_LDS(ld + mxg::A_BYTES + (wv * mxg::NB + (d - mxg::NA)) * 1024), 16, 0, 0);
@@ -223,7 +231,7 @@ __device__ __forceinline__ void mx_step(const MxCtx &c, int k0, int wv,
     sb[j] = *reinterpret_cast<const uint32_t *>(rd + c.sb_lds[j]) >> gsh;
   i32x8_t fra[mxg::TM], frb[2][mxg::TN];
 #pragma unroll
-  for (int i = 0; i < mxg::TM; ++i) fra[i] = frag(c.fa[i], 0);
+  for (int i = 0; i < VT; ++i) fra[i] = frag(c.fa[i], 0);
 #pragma unroll
   for (int j = 0; j < mxg::TN; ++j) frb[0][j] = frag(c.fb[j], 0);
   __builtin_amdgcn_sched_barrier(0);
@@ -234,15 +242,17 @@ __device__ __forceinline__ void mx_step(const MxCtx &c, int k0, int wv,
     for (int q = 0; q < mxg::TM * mxg::TN; ++q) {
       const int gi = ks * mxg::TM * mxg::TN + q;
       const int i = q / mxg::TN, j = q % mxg::TN;
-      if (ks == 0)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fra[i], frb[cur][j], acc[i][j], 0, 0, 0, (int)sa[i], 0, (int)sb[j]);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fra[i], frb[cur][j], acc[i][j], 0, 0, 2, (int)sa[i], 2, (int)sb[j]);
+      if (i < VT) {
+        if (ks == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fra[i], frb[cur][j], acc[i][j], 0, 0, 0, (int)sa[i], 0, (int)sb[j]);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fra[i], frb[cur][j], acc[i][j], 0, 0, 2, (int)sa[i], 2, (int)sb[j]);
+      }
       if (ks + 1 < mxg::KS) {
         if (q < mxg::TN) frb[cur ^ 1][q] = frag(c.fb[q], ks + 1);
-        if (j == mxg::TN - 1) fra[i] = frag(c.fa[i], ks + 1);
+        if (j == mxg::TN - 1 && i < VT) fra[i] = frag(c.fa[i], ks + 1);
       }
       if (gi % GAP == 0 && gi / GAP < L) issue_one(gi / GAP);
       __builtin_amdgcn_sched_barrier(0);
@@ -343,17 +353,36 @@ __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int nk = Kdim / mxg::BK;
+  // this wave's valid 32-row MFMA tiles and the A loads that feed only rows
+  // past the last valid 32-row group of the tile (wave-uniform)
+  const int nvalid = min(mxg::BM, tl.row_end - tl.row0);
+  const int vt = __builtin_amdgcn_readfirstlane(min(mxg::TM, max(0, (nvalid - wm * 128 + 31) / 32)));
+  c.a_skip = 0;
+#pragma unroll
+  for (int i = 0; i < mxg::NA; ++i)
+    if ((wv * mxg::NA + i) * mxg::RPI >= ((nvalid + 31) / 32) * 32) c.a_skip |= 1u << i;
+  c.a_skip = __builtin_amdgcn_readfirstlane(c.a_skip);
   mx_issue(c, 0, wv, smem);
-  for (int kb = 0; kb < nk; ++kb) {
-    wait_vmcnt<0>();                    // this wave's loads of step kb have landed ...
-    __builtin_amdgcn_s_barrier();       // ... and every wave's
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    uint8_t *ld = smem + ((kb + 1) & 1) * mxg::STAGE;
-    const uint8_t *rd = smem + (kb & 1) * mxg::STAGE;
-    // the next step's loads; the last iteration reloads its own step into the
-    // idle stage (in bounds, never read: the epilogue's barrier drains it)
-    mx_step(c, min(kb + 1, nk - 1) * mxg::BK, wv, ld, rd, g, acc);
+  auto main_loop = [&](auto vt_tag) {
+    constexpr int VT = decltype(vt_tag)::value;
+    for (int kb = 0; kb < nk; ++kb) {
+      wait_vmcnt<0>();                    // this wave's loads of step kb have landed ...
+      __builtin_amdgcn_s_barrier();       // ... and every wave's
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      uint8_t *ld = smem + ((kb + 1) & 1) * mxg::STAGE;
+      const uint8_t *rd = smem + (kb & 1) * mxg::STAGE;
+      // the next step's loads; the last iteration reloads its own step into
+      // the idle stage (in bounds, never read: the epilogue's barrier drains it)
+      mx_step<VT>(c, min(kb + 1, nk - 1) * mxg::BK, wv, ld, rd, g, acc);
+    }
+  };
+  switch (vt) {
+    case 4: main_loop(std::integral_constant<int, 4>{}); break;
+    case 3: main_loop(std::integral_constant<int, 3>{}); break;
+    case 2: main_loop(std::integral_constant<int, 2>{}); break;
+    case 1: main_loop(std::integral_constant<int, 1>{}); break;
+    default: main_loop(std::integral_constant<int, 0>{}); break;
   }
 
   // Epilogue through LDS (the forward's): neighbouring lanes swap one value
