@@ -410,18 +410,14 @@ __device__ __forceinline__ const uint16_t *big_b_src(const BigCtx &c, int i, int
 }
 
 template <int MODE>
-__device__ __forceinline__ void big_issue(const BigCtx &c, int k0, int wv,
-                                          uint8_t *__restrict__ stage) {
+__device__ __forceinline__ void big_issue(const BigCtx &c, int k0, int wv, uint32_t stage) {
 #pragma unroll
   for (int i = 0; i < bt::LPW; ++i)
     if (!((c.a_skip >> i) & 1))
-      __builtin_amdgcn_global_load_lds(big_a_src<MODE>(c, i, k0),
-                                       MOE_LDS(stage + (wv * bt::LPW + i) * 1024), 16, 0, 0);
+      dma16(big_a_src<MODE>(c, i, k0), stage + (wv * bt::LPW + i) * 1024);
 #pragma unroll
   for (int i = 0; i < bt::LPW; ++i)
-    __builtin_amdgcn_global_load_lds(big_b_src<MODE>(c, i, k0),
-                                     MOE_LDS(stage + bt::TILE + (wv * bt::LPW + i) * 1024), 16,
-                                     0, 0);
+    dma16(big_b_src<MODE>(c, i, k0), stage + bt::TILE + (wv * bt::LPW + i) * 1024);
 }
 
 // One main-loop step (see the forward's big_step): MFMAs of this step from
@@ -431,7 +427,7 @@ __device__ __forceinline__ void big_issue(const BigCtx &c, int k0, int wv,
 // last tile: the others' MFMAs and A fragment reads are dropped).
 template <int MODE, int VT>
 __device__ __forceinline__ void big_step(const BigCtx &c, int k0, bool do_load, int wv,
-                                         uint8_t *__restrict__ ld, const uint8_t *__restrict__ rd,
+                                         uint32_t ld, const uint8_t *__restrict__ rd,
                                          int khalf, f32x16_t (&acc)[bt::TM][bt::TN]) {
   constexpr int MF = bt::KS * bt::TM * bt::TN;   // 32 MFMAs per step
   constexpr int L = 2 * bt::LPW;                 // 8 direct loads per step
@@ -439,12 +435,9 @@ __device__ __forceinline__ void big_step(const BigCtx &c, int k0, bool do_load, 
   auto issue_one = [&](int d) {
     if (d < bt::LPW) {
       if (VT == bt::TM || !((c.a_skip >> d) & 1))
-        __builtin_amdgcn_global_load_lds(big_a_src<MODE>(c, d, k0),
-                                         MOE_LDS(ld + (wv * bt::LPW + d) * 1024), 16, 0, 0);
+        dma16(big_a_src<MODE>(c, d, k0), ld + (wv * bt::LPW + d) * 1024);
     } else
-      __builtin_amdgcn_global_load_lds(big_b_src<MODE>(c, d - bt::LPW, k0),
-                                       MOE_LDS(ld + bt::TILE + (wv * bt::LPW + d - bt::LPW) * 1024),
-                                       16, 0, 0);
+      dma16(big_b_src<MODE>(c, d - bt::LPW, k0), ld + bt::TILE + (wv * bt::LPW + d - bt::LPW) * 1024);
   };
   bf16x8_t fra[2][bt::TM], frb[2][bt::TN];
   auto read_frag = [&](int buf, int ks, int q) {
@@ -556,7 +549,8 @@ __global__ __launch_bounds__(bt::NT, 1) void k_gemm_bwd_big(GemmArgs p) {
       if ((wv * bt::LPW + i) * 8 >= ((nvalid + 31) / 32) * 32) c.a_skip |= 1u << i;
   }
   c.a_skip = __builtin_amdgcn_readfirstlane(c.a_skip);
-  if (nk > 0) big_issue<MODE>(c, 0, wv, smem);
+  const uint32_t smem_l = lds_addr(smem);
+  if (nk > 0) big_issue<MODE>(c, 0, wv, smem_l);
   // one main loop per count of valid 32-row tiles of this wave
   auto main_loop = [&](auto vt_tag) {
     constexpr int VT = decltype(vt_tag)::value;
@@ -565,7 +559,7 @@ __global__ __launch_bounds__(bt::NT, 1) void k_gemm_bwd_big(GemmArgs p) {
       __builtin_amdgcn_s_barrier();   // ... and so have every wave's
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      uint8_t *ld = smem + ((kb + 1) & 1) * bt::STAGE;   // read in step kb-1: free now
+      const uint32_t ld = smem_l + ((kb + 1) & 1) * bt::STAGE;   // read in step kb-1: free now
       uint8_t *rd = smem + (kb & 1) * bt::STAGE;
       if (MODE == BW_WG && kb == nk - 1 && rem != 0) {
         // rows past the expert's range contribute nothing: zero them in B
@@ -584,6 +578,7 @@ __global__ __launch_bounds__(bt::NT, 1) void k_gemm_bwd_big(GemmArgs p) {
     case 1: main_loop(std::integral_constant<int, 1>{}); break;
     default: main_loop(std::integral_constant<int, 0>{}); break;
   }
+  wait_vmcnt<0>();   // no direct load still in flight into the stages
 
   // ---- epilogues. MFMA result layout: register r of lane l holds row
   // 8*(r/4) + 4*(l/32) + r%4, column l%32 of its 32 x 32 tile.

@@ -284,18 +284,32 @@ template <int BM, int BK, int NS, int NW>
 __device__ __forceinline__ void big_issue(const uint16_t *__restrict__ A,
                                           const uint16_t *__restrict__ Wj, const uint32_t *a_off,
                                           const uint32_t *b_off, int k0, int wv,
-                                          uint8_t *__restrict__ stage) {
+                                          uint32_t stage) {
   using P = BigTile<BM, BK, NS, NW>;
 #pragma unroll
-  for (int i = 0; i < P::NA; ++i)
-    __builtin_amdgcn_global_load_lds(A + a_off[i] + k0,
-                                     MOE_LDS(stage + (wv * P::NA + i) * 1024), 16, 0, 0);
+  for (int i = 0; i < P::NA; ++i) dma16(A + a_off[i] + k0, stage + (wv * P::NA + i) * 1024);
 #pragma unroll
   for (int i = 0; i < P::NB; ++i)
-    __builtin_amdgcn_global_load_lds(Wj + b_off[i] + k0,
-                                     MOE_LDS(stage + P::A_BYTES + (wv * P::NB + i) * 1024), 16,
-                                     0, 0);
+    dma16(Wj + b_off[i] + k0, stage + P::A_BYTES + (wv * P::NB + i) * 1024);
 }
+
+// Order in which a sub-step's fragments are read: the order of their first
+// use by the MFMA sequence (A0 B0 B1 A1 A2 A3 for 4 x 2 tiles), so that the
+// MFMAs at the start of a sub-step wait only for the oldest reads.
+template <int TM, int TN>
+struct FragOrder {
+  int q[TM + TN];
+  constexpr FragOrder() : q() {
+    bool seen[TM + TN] = {};
+    int n = 0;
+    for (int m = 0; m < TM * TN; ++m) {
+      const int a = m / TN, b = TM + m % TN;
+      if (!seen[a]) { seen[a] = true; q[n++] = a; }
+      if (!seen[b]) { seen[b] = true; q[n++] = b; }
+    }
+  }
+};
+
 
 // One main-loop step: run the MFMAs of this K step from `rd` while issuing
 // the direct loads of a later K step into `ld`. The stages are restrict
@@ -308,7 +322,9 @@ __device__ __forceinline__ void big_issue(const uint16_t *__restrict__ A,
 //     address path is fed steadily instead of stalling issue at step start;
 //   * fragments double-buffered across the K sub-steps: each read of
 //     sub-step ks+1 follows one MFMA of sub-step ks, so it lands while the
-//     remaining MFMAs of ks execute.
+//     remaining MFMAs of ks execute; reads go in first-use order, and the
+//     direct loads are inline asm (dma16), so each MFMA waits only for the
+//     reads it needs.
 //
 // VT < TM (the last m-tile of an expert): only this wave's first VT 32-row
 // MFMA tiles hold valid rows; the MFMAs and A fragment reads of the others are
@@ -318,29 +334,29 @@ __device__ __forceinline__ void big_issue(const uint16_t *__restrict__ A,
 template <bool GATE_UP, int BM, int BK, int NS, int NW, int VT = BigTile<BM, BK, NS, NW>::TM>
 __device__ __forceinline__ void big_step(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ Wj, const uint32_t *a_off,
-    const uint32_t *b_off, int k0, bool do_load, int wv, uint8_t *__restrict__ ld,
+    const uint32_t *b_off, int k0, int wv, uint32_t ldl,
     const uint8_t *__restrict__ rd, const int *fa, const int *fb, int khalf, int sw,
     f32x16_t (&acc)[BigTile<BM, BK, NS, NW>::TM][BigTile<BM, BK, NS, NW>::TN],
+    bf16x8_t (&fra)[2][BigTile<BM, BK, NS, NW>::TM], bf16x8_t (&frb)[2][BigTile<BM, BK, NS, NW>::TN],
     uint32_t a_skip = 0) {
   using P = BigTile<BM, BK, NS, NW>;
   constexpr bool PARTIAL = VT < P::TM;
   constexpr int MF = P::KS * P::TM * P::TN;      // MFMAs per step
+  constexpr int MS = P::TM * P::TN;              // MFMAs per sub-step
   // MFMAs between two direct loads: spread over the step, or over its first
   // half with two stages (those loads must land before the next step)
   constexpr int GAP = (NS == 2 && MF >= 2 * P::L) ? MF / (2 * P::L) : MF / P::L;
   static_assert(GAP >= 1 && GAP * P::L <= MF, "load spacing");
+  constexpr FragOrder<P::TM, P::TN> ord{};
   auto issue_one = [&](int d) {
     if (d < P::NA) {
       if (!PARTIAL || !((a_skip >> d) & 1))
-        __builtin_amdgcn_global_load_lds(A + a_off[d] + k0,
-                                         MOE_LDS(ld + (wv * P::NA + d) * 1024), 16, 0, 0);
+        dma16(A + a_off[d] + k0, ldl + (wv * P::NA + d) * 1024);
     } else
-      __builtin_amdgcn_global_load_lds(
-          Wj + b_off[d - P::NA] + k0,
-          MOE_LDS(ld + P::A_BYTES + (wv * P::NB + (d - P::NA)) * 1024), 16, 0, 0);
+      dma16(Wj + b_off[d - P::NA] + k0, ldl + P::A_BYTES + (wv * P::NB + (d - P::NA)) * 1024);
   };
-  bf16x8_t fra[2][P::TM], frb[2][P::TN];
-  auto read_frag = [&](int buf, int ks, int q) {
+  auto read_frag = [&](int buf, int ks, int r) {
+    const int q = ord.q[r];
     const int cb = ((ks * 2 + khalf) ^ sw) << 4;
     if (q < P::TM) {
       if (q < VT)
@@ -348,21 +364,24 @@ __device__ __forceinline__ void big_step(
     } else
       frb[buf][q - P::TM] = *reinterpret_cast<const bf16x8_t *>(rd + fb[q - P::TM] + cb);
   };
+  auto mfma = [&](int buf, int q) {
+    const int i = q / P::TN, j = q % P::TN;
+    if (i < VT)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fra[buf][i], frb[buf][j], acc[i][j],
+                                                          0, 0, 0);
+  };
 #pragma unroll
-  for (int q = 0; q < P::TM + P::TN; ++q) read_frag(0, 0, q);
+  for (int r = 0; r < P::TM + P::TN; ++r) read_frag(0, 0, r);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ks = 0; ks < P::KS; ++ks) {
     const int cur = ks & 1;
 #pragma unroll
-    for (int q = 0; q < P::TM * P::TN; ++q) {
-      const int g = ks * P::TM * P::TN + q;
-      const int i = q / P::TN, j = q % P::TN;
-      if (i < VT)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fra[cur][i], frb[cur][j], acc[i][j],
-                                                            0, 0, 0);
+    for (int q = 0; q < MS; ++q) {
+      const int g = ks * MS + q;
+      mfma(cur, q);
       if (ks + 1 < P::KS && q < P::TM + P::TN) read_frag(cur ^ 1, ks + 1, q);
-      if (do_load && g % GAP == 0 && g / GAP < P::L) issue_one(g / GAP);
+      if (g % GAP == 0 && g / GAP < P::L) issue_one(g / GAP);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -376,12 +395,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
   using P = BigTile<BM, BK, NS, NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * P::STAGE_BYTES];
 
+  const uint32_t smem_l = lds_addr(smem);
   const Tile tl = find_tile<MOE_TILE_NGROUP>(off, E_L, BM, n_tiles_n);
   if (!tl.valid) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv / P::WAVES_N, wn = wv % P::WAVES_N;
   const int Nw = GATE_UP ? 2 * Nout : Nout;
   const uint16_t *Wj = W + (size_t)tl.expert * Nw * Kdim;
@@ -441,17 +461,21 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
   const int nvalid = min(BM, tl.row_end - tl.row0);
   const int vt = __builtin_amdgcn_readfirstlane(min(P::TM, max(0, (nvalid - wm * 128 + 31) / 32)));
   uint32_t a_skip = 0;
+  // (with more than two stages the vmcnt waits count a fixed number of loads
+  // per step, so no load is skipped)
 #pragma unroll
   for (int i = 0; i < P::NA; ++i)
-    if ((wv * P::NA + i) * P::RPI >= ((nvalid + 31) / 32) * 32) a_skip |= 1u << i;
+    if (NS == 2 && (wv * P::NA + i) * P::RPI >= ((nvalid + 31) / 32) * 32) a_skip |= 1u << i;
   a_skip = __builtin_amdgcn_readfirstlane(a_skip);
   // prologue: K steps 0 .. NS-2 into stages 0 .. NS-2
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk)
-      big_issue<BM, BK, NS, NW>(A, Wj, a_off, b_off, s * BK, wv, smem + s * P::STAGE_BYTES);
+      big_issue<BM, BK, NS, NW>(A, Wj, a_off, b_off, s * BK, wv,
+                                smem_l + s * P::STAGE_BYTES);
   // one main loop per count of valid 32-row tiles of this wave (TM for full
   // tiles; fewer on an expert's last m-tile), each with a single inlined step
+  bf16x8_t fra[2][P::TM], frb[2][P::TN];
   auto main_loop = [&](auto vt_tag) {
     constexpr int VT = decltype(vt_tag)::value;
     for (int kb = 0; kb < nk; ++kb) {
@@ -463,11 +487,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       const int ls = (kb + NS - 1) % NS;   // stage read in step kb-1: free after the barrier
-      uint8_t *ld = smem + ls * P::STAGE_BYTES;
+      const uint32_t ldl = smem_l + ls * P::STAGE_BYTES;
       const uint8_t *rd = smem + (kb % NS) * P::STAGE_BYTES;
-      big_step<GATE_UP, BM, BK, NS, NW, VT>(A, Wj, a_off, b_off, (kb + NS - 1) * BK,
-                                            kb + NS - 1 < nk, wv, ld, rd, fa, fb, khalf, sw, acc,
-                                            a_skip);
+      // the last NS-1 steps reload the last K step into stages no longer
+      // read, so every step issues the same loads (no branch around them)
+      big_step<GATE_UP, BM, BK, NS, NW, VT>(A, Wj, a_off, b_off, min(kb + NS - 1, nk - 1) * BK,
+                                            wv, ldl, rd, fa, fb, khalf, sw, acc, fra, frb, a_skip);
     }
   };
   static_assert(P::TM == 4, "main-loop variants");
@@ -495,6 +520,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
   constexpr int OUTC = GATE_UP ? P::BW / 2 : P::BW;    // output columns per block
   constexpr int ROWB = OUTC * 2;                       // bytes per staged row
   static_assert(BM * ROWB <= NS * P::STAGE_BYTES, "epilogue tile fits the stages");
+  wait_vmcnt<0>();   // no direct load still in flight into the stages
   __syncthreads();   // every wave is done reading the last stage
   auto stage_off = [](int row, int colb) {   // byte offset of (row, byte column)
     const int q = (row & 1) | (((row >> 2) & 1) << 1);

@@ -20,6 +20,28 @@ __device__ __forceinline__ int chunk_swz(int r) {
 
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
+// Direct global -> LDS loads (lane l's SZ bytes land at LDS byte address
+// lds + SZ * l; lds wave-uniform). Written as inline asm rather than the
+// compiler builtin: the compiler counts the builtin as an LDS event of its own
+// kind, which turns every wait for the fragment reads (ds_read) into a full
+// lgkmcnt(0); the asm form leaves those waits exact. The loads are then
+// invisible to the compiler's own vmcnt bookkeeping: the kernels order them
+// with explicit wait_vmcnt + s_barrier (and wait_vmcnt<0> before any other
+// use of the LDS they write).
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+__device__ __forceinline__ void dma4(const void *gptr, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)MOE_LDS(p);
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
 template <int N>

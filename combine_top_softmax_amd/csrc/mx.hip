@@ -163,20 +163,15 @@ struct MxCtx {
   uint32_t a_skip;            // A loads that feed only rows past the valid ones
 };
 
-__device__ __forceinline__ void mx_issue(const MxCtx &c, int k0, int wv,
-                                         uint8_t *__restrict__ stage) {
-  __builtin_amdgcn_global_load_lds(c.S + (uint32_t)(c.s_off + (k0 >> 5)), MOE_LDS(stage + c.s_dst),
-                                   4, 0, 0);
+__device__ __forceinline__ void mx_issue(const MxCtx &c, int k0, int wv, uint32_t stage) {
+  dma4(c.S + (uint32_t)(c.s_off + (k0 >> 5)), stage + c.s_dst);
 #pragma unroll
   for (int i = 0; i < mxg::NA; ++i)
     if (!((c.a_skip >> i) & 1))
-      __builtin_amdgcn_global_load_lds(c.A + (uint32_t)(c.a_off[i] + k0),
-                                       MOE_LDS(stage + (wv * mxg::NA + i) * 1024), 16, 0, 0);
+      dma16(c.A + (uint32_t)(c.a_off[i] + k0), stage + (wv * mxg::NA + i) * 1024);
 #pragma unroll
   for (int i = 0; i < mxg::NB; ++i)
-    __builtin_amdgcn_global_load_lds(c.W + (uint32_t)(c.b_off[i] + k0),
-                                     MOE_LDS(stage + mxg::A_BYTES + (wv * mxg::NB + i) * 1024), 16,
-                                     0, 0);
+    dma16(c.W + (uint32_t)(c.b_off[i] + k0), stage + mxg::A_BYTES + (wv * mxg::NB + i) * 1024);
 }
 
 // One main-loop step: 2 x 8 scaled MFMAs from `rd`, the direct loads of the
@@ -190,7 +185,7 @@ __device__ __forceinline__ void mx_issue(const MxCtx &c, int k0, int wv,
 // expert's last m-tile: the others' MFMAs and A fragment reads are dropped).
 template <int VT>
 __device__ __forceinline__ void mx_step(const MxCtx &c, int k0, int wv,
-                                        uint8_t *__restrict__ ld, const uint8_t *__restrict__ rd,
+                                        uint32_t ld, const uint8_t *__restrict__ rd,
                                         int g, f32x16_t (&acc)[mxg::TM][mxg::TN]) {
   constexpr int MF = mxg::KS * mxg::TM * mxg::TN;   // 16
   constexpr int L = mxg::L + 1;                     // + the scale load
@@ -200,15 +195,12 @@ __device__ __forceinline__ void mx_step(const MxCtx &c, int k0, int wv,
   auto issue_one = [&](int d) {
     if (d < mxg::NA) {
       if (VT == mxg::TM || !((c.a_skip >> d) & 1))
-        __builtin_amdgcn_global_load_lds(c.A + (uint32_t)(c.a_off[d] + k0),
-                                         MOE_LDS(ld + (wv * mxg::NA + d) * 1024), 16, 0, 0);
+        dma16(c.A + (uint32_t)(c.a_off[d] + k0), ld + (wv * mxg::NA + d) * 1024);
     } else if (d < mxg::L)
-      __builtin_amdgcn_global_load_lds(
-          c.W + (uint32_t)(c.b_off[d - mxg::NA] + k0),
-          MOE_LDS(ld + mxg::A_BYTES + (wv * mxg::NB + (d - mxg::NA)) * 1024), 16, 0, 0);
+      dma16(c.W + (uint32_t)(c.b_off[d - mxg::NA] + k0),
+            ld + mxg::A_BYTES + (wv * mxg::NB + (d - mxg::NA)) * 1024);
     else
-      __builtin_amdgcn_global_load_lds(c.S + (uint32_t)(c.s_off + (k0 >> 5)), MOE_LDS(ld + c.s_dst),
-                                       4, 0, 0);
+      dma4(c.S + (uint32_t)(c.s_off + (k0 >> 5)), ld + c.s_dst);
   };
   // chunks g and 2 + g of the 64-byte K slice ks of LDS row `off`
   auto frag = [&](int off, int ks) {
@@ -362,7 +354,8 @@ __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
   for (int i = 0; i < mxg::NA; ++i)
     if ((wv * mxg::NA + i) * mxg::RPI >= ((nvalid + 31) / 32) * 32) c.a_skip |= 1u << i;
   c.a_skip = __builtin_amdgcn_readfirstlane(c.a_skip);
-  mx_issue(c, 0, wv, smem);
+  const uint32_t smem_l = lds_addr(smem);
+  mx_issue(c, 0, wv, smem_l);
   auto main_loop = [&](auto vt_tag) {
     constexpr int VT = decltype(vt_tag)::value;
     for (int kb = 0; kb < nk; ++kb) {
@@ -370,10 +363,10 @@ __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
       __builtin_amdgcn_s_barrier();       // ... and every wave's
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      uint8_t *ld = smem + ((kb + 1) & 1) * mxg::STAGE;
+      const uint32_t ld = smem_l + ((kb + 1) & 1) * mxg::STAGE;
       const uint8_t *rd = smem + (kb & 1) * mxg::STAGE;
       // the next step's loads; the last iteration reloads its own step into
-      // the idle stage (in bounds, never read: the epilogue's barrier drains it)
+      // the idle stage (in bounds, never read; drained before the epilogue)
       mx_step<VT>(c, min(kb + 1, nk - 1) * mxg::BK, wv, ld, rd, g, acc);
     }
   };
@@ -384,6 +377,7 @@ __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
     case 1: main_loop(std::integral_constant<int, 1>{}); break;
     default: main_loop(std::integral_constant<int, 0>{}); break;
   }
+  wait_vmcnt<0>();   // no direct load still in flight into the stages
 
   // Epilogue through LDS (the forward's): neighbouring lanes swap one value
   // (DPP) so each writes two adjacent columns of one row as a bf16x2 dword;
