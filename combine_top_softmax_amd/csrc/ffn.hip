@@ -108,11 +108,17 @@ __device__ __forceinline__ Tile find_tile(const int32_t *__restrict__ off, int E
 // n-tiles per group in the tile order (1 = all m-tiles of one n-tile, then the
 // next n-tile): equal or best on every named workload among 1, 2, 4, 8 and
 // "all n-tiles of an m-tile first".
-// Waves per big-tile block: 8 (two per SIMD, 128 x 64 wave tiles, 128
-// accumulators each) measured 1-7% faster than 4 (one per SIMD, 128 x 128
-// wave tiles): twice as many waves keep operand loads in flight.
+// Waves per big-tile block: 4 (one per SIMD, 128 x 128 wave tiles, 256
+// accumulators each) measured 2-5% faster than 8 (two per SIMD, 128 x 64
+// wave tiles) on the named workloads once the fragment-read waits were exact:
+// square wave tiles read a third fewer bytes from LDS per flop, and this
+// kernel runs power-limited (the shader clock drops to ~1.3-1.6 GHz in its
+// main loop), so less data movement buys clock.
 #ifndef MOE_GEMM_WAVES
-#define MOE_GEMM_WAVES 8
+#define MOE_GEMM_WAVES 4
+#endif
+#ifndef MOE_BSTAGES
+#define MOE_BSTAGES 3
 #endif
 #ifndef MOE_TILE_NGROUP
 #define MOE_TILE_NGROUP 1
@@ -243,17 +249,21 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(
 }
 
 // ------------------------------------------------------------ bf16 MFMA, big tiles
-// Block tile BM rows x 256 weight rows, K step BK, NS LDS stages, NW waves
-// (the library instantiates BM = 256, BK = 64, NS = 2, NW = 8; the template
-// also covers BM = 128, BK = 32 and NW = 4, which measured slower):
+// Block tile BM rows x 256 weight rows, K step BK, two LDS stages for the A
+// rows and NS (2 or 3) for the weight rows, NW waves (the library
+// instantiates BM = 256, BK = 64, NS = 3, NW = 4; the template also covers
+// BM = 128, BK = 32 and NW = 8, which measured slower):
 //   NW = 8, BM = 256: 2 x 4 waves of 128 x 64 (4 x 2 MFMA tiles, 128 accumulators)
 //   NW = 4, BM = 256: 2 x 2 waves of 128 x 128 (4 x 4 MFMA tiles, 256 accumulators)
 // Operands go global -> LDS directly (global_load_lds_dwordx4, no VGPR
-// staging). The loads of K step k + NS - 1 are issued right after the barrier
-// that opens step k, so each load has NS - 1 steps of MFMA work to land; the
-// barrier is a plain s_barrier preceded by a wait for this wave's loads of the
-// step about to be read (s_waitcnt vmcnt(N) with N = loads still allowed in
-// flight), not a full fence that would drain every outstanding load.
+// staging). Step k, right after its opening barrier, issues the A loads of
+// step k + 1 and then the weight loads of step k + NS - 1: the weight rows
+// (each read from HBM once per expert, shared by fewer tiles than the A rows)
+// get NS - 1 steps of MFMA work to land, the A rows one (2 x 32 KiB + 3 x 32
+// KiB fill the 160 KiB of LDS). The barrier is a plain s_barrier preceded by
+// a wait for this wave's loads of the step about to be read (s_waitcnt
+// vmcnt(N) with N = the younger weight loads still allowed in flight), not a
+// full fence that would drain every outstanding load.
 // LDS rows are BK bf16 (BK/8 16-byte chunks); chunk c of row r is stored at
 // c ^ swz(r), chosen so that a wave's direct load writes whole rows
 // contiguously and the fragment reads of 16 consecutive rows (one chunk each)
@@ -274,7 +284,8 @@ struct BigTile {
   static constexpr int NB = BW / RPI / NW;       // B direct loads per wave per step
   static constexpr int L = NA + NB;
   static constexpr int KS = BK / 16;             // MFMA K sub-steps per step
-  static constexpr int A_BYTES = BM * ROW_B;
+  static constexpr int A_BYTES = BM * ROW_B;     // one A stage
+  static constexpr int B_BYTES = BW * ROW_B;     // one B stage
   static constexpr int STAGE_BYTES = (BM + BW) * ROW_B;
 };
 
@@ -283,14 +294,15 @@ struct BigTile {
 template <int BM, int BK, int NS, int NW>
 __device__ __forceinline__ void big_issue(const uint16_t *__restrict__ A,
                                           const uint16_t *__restrict__ Wj, const uint32_t *a_off,
-                                          const uint32_t *b_off, int k0, int wv,
-                                          uint32_t stage) {
+                                          const uint32_t *b_off, int ka, int kb, int wv,
+                                          uint32_t sa, uint32_t sb, bool do_a) {
   using P = BigTile<BM, BK, NS, NW>;
+  if (do_a) {
 #pragma unroll
-  for (int i = 0; i < P::NA; ++i) dma16(A + a_off[i] + k0, stage + (wv * P::NA + i) * 1024);
+    for (int i = 0; i < P::NA; ++i) dma16(A + a_off[i] + ka, sa + (wv * P::NA + i) * 1024);
+  }
 #pragma unroll
-  for (int i = 0; i < P::NB; ++i)
-    dma16(Wj + b_off[i] + k0, stage + P::A_BYTES + (wv * P::NB + i) * 1024);
+  for (int i = 0; i < P::NB; ++i) dma16(Wj + b_off[i] + kb, sb + (wv * P::NB + i) * 1024);
 }
 
 // Order in which a sub-step's fragments are read: the order of their first
@@ -334,8 +346,9 @@ struct FragOrder {
 template <bool GATE_UP, int BM, int BK, int NS, int NW, int VT = BigTile<BM, BK, NS, NW>::TM>
 __device__ __forceinline__ void big_step(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ Wj, const uint32_t *a_off,
-    const uint32_t *b_off, int k0, int wv, uint32_t ldl,
-    const uint8_t *__restrict__ rd, const int *fa, const int *fb, int khalf, int sw,
+    const uint32_t *b_off, int ka, int kb, int wv, uint32_t lda, uint32_t ldb,
+    const uint8_t *__restrict__ rda, const uint8_t *__restrict__ rdb, const int *fa,
+    const int *fb, int khalf, int sw,
     f32x16_t (&acc)[BigTile<BM, BK, NS, NW>::TM][BigTile<BM, BK, NS, NW>::TN],
     bf16x8_t (&fra)[2][BigTile<BM, BK, NS, NW>::TM], bf16x8_t (&frb)[2][BigTile<BM, BK, NS, NW>::TN],
     uint32_t a_skip = 0) {
@@ -351,18 +364,18 @@ __device__ __forceinline__ void big_step(
   auto issue_one = [&](int d) {
     if (d < P::NA) {
       if (!PARTIAL || !((a_skip >> d) & 1))
-        dma16(A + a_off[d] + k0, ldl + (wv * P::NA + d) * 1024);
+        dma16(A + a_off[d] + ka, lda + (wv * P::NA + d) * 1024);
     } else
-      dma16(Wj + b_off[d - P::NA] + k0, ldl + P::A_BYTES + (wv * P::NB + (d - P::NA)) * 1024);
+      dma16(Wj + b_off[d - P::NA] + kb, ldb + (wv * P::NB + (d - P::NA)) * 1024);
   };
   auto read_frag = [&](int buf, int ks, int r) {
     const int q = ord.q[r];
     const int cb = ((ks * 2 + khalf) ^ sw) << 4;
     if (q < P::TM) {
       if (q < VT)
-        fra[buf][q] = *reinterpret_cast<const bf16x8_t *>(rd + fa[q] + cb);
+        fra[buf][q] = *reinterpret_cast<const bf16x8_t *>(rda + fa[q] + cb);
     } else
-      frb[buf][q - P::TM] = *reinterpret_cast<const bf16x8_t *>(rd + fb[q - P::TM] + cb);
+      frb[buf][q - P::TM] = *reinterpret_cast<const bf16x8_t *>(rdb + fb[q - P::TM] + cb);
   };
   auto mfma = [&](int buf, int q) {
     const int i = q / P::TN, j = q % P::TN;
@@ -387,13 +400,90 @@ __device__ __forceinline__ void big_step(
   }
 }
 
+// Epilogue of the big-tile kernels (every wave past its last MFMA, every
+// direct load drained, the stages free).
+template <bool GATE_UP, int BM, int NW>
+__device__ __forceinline__ void big_epilogue(
+    const f32x16_t (&acc)[BigTile<BM, 64, 2, NW>::TM][BigTile<BM, 64, 2, NW>::TN],
+    uint8_t *__restrict__ smem, const Tile &tl, uint16_t *__restrict__ Out, int Nout, int n0,
+    int wm, int wn) {
+  using P = BigTile<BM, 64, 2, NW>;
+  // Epilogue, staged through LDS so that global stores are whole 16-byte
+  // vectors along output rows (the MFMA result layout gives each lane one
+  // column: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
+  // of its 32x32 tile).
+  //  1. neighbouring lanes swap one value (DPP quad permute 1,0,3,2) so each
+  //     lane holds two adjacent columns of one row and writes them as one
+  //     bf16x2 dword into a row-major LDS tile;
+  //  2. every thread copies 16-byte chunks of the tile to global memory,
+  //     skipping rows past the expert's last valid row and columns past Nout.
+  // LDS rows are OUTC bf16; 16-byte chunk c of row r sits at c ^ (4 * q(r))
+  // with q(r) = bit0(r) | bit2(r) << 1, so the four rows one dword write
+  // instruction touches (R, R+1, R+4, R+5) land in four distinct 64-byte
+  // bank groups.
+  constexpr int OUTC = GATE_UP ? P::BW / 2 : P::BW;    // output columns per block
+  constexpr int ROWB = OUTC * 2;                       // bytes per staged row
+  static_assert(BM * ROWB <= 2 * P::A_BYTES + 2 * P::B_BYTES, "epilogue tile fits the stages");
+  const int tid = threadIdx.x, lane = tid & 63, fr = lane & 31, khalf = lane >> 5;
+  auto stage_off = [](int row, int colb) {   // byte offset of (row, byte column)
+    const int q = (row & 1) | (((row >> 2) & 1) << 1);
+    return row * ROWB + ((((colb >> 4) ^ (q << 2))) << 4) + (colb & 15);
+  };
+  const bool odd = (lane & 1) != 0;
+#pragma unroll
+  for (int tm = 0; tm < P::TM; ++tm) {
+#pragma unroll
+    for (int tn = 0; tn < (GATE_UP ? P::TN / 2 : P::TN); ++tn) {
+      const int colb0 = (GATE_UP ? wn * (P::WTN / 2) : wn * P::WTN) * 2 + tn * 64;  // tile col * 2
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float v0, v1;
+        if (GATE_UP) {
+          const float g0 = acc[tm][tn][r], u0 = acc[tm][tn + P::TN / 2][r];
+          const float g1 = acc[tm][tn][r + 1], u1 = acc[tm][tn + P::TN / 2][r + 1];
+          v0 = g0 * __builtin_amdgcn_rcpf(1.0f + __expf(-g0)) * u0;
+          v1 = g1 * __builtin_amdgcn_rcpf(1.0f + __expf(-g1)) * u1;
+        } else {
+          v0 = acc[tm][tn][r];
+          v1 = acc[tm][tn][r + 1];
+        }
+        // even lane keeps row r and takes its partner's row-r value; odd
+        // lane keeps row r+1 and takes its partner's row-(r+1) value
+        const float send = odd ? v0 : v1;
+        const float recv = __int_as_float(
+            __builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
+        const int row = wm * 128 + tm * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3) + (odd ? 1 : 0);
+        const int colb = colb0 + (fr & ~1) * 2;
+        const uint32_t packed = odd ? pack_bf16x2(recv, v1) : pack_bf16x2(v0, recv);
+        *reinterpret_cast<uint32_t *>(smem + stage_off(row, colb)) = packed;
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int CPR = ROWB / 16;                        // 16-byte chunks per row
+  const int ncols = min(OUTC, Nout - n0);               // multiple of 8
+  const int nrows = min(BM, tl.row_end - tl.row0);
+#pragma unroll 4
+  for (int idx = tid; idx < BM * CPR; idx += 64 * NW) {
+    const int row = idx / CPR, ch = idx % CPR;
+    if (row < nrows && ch * 8 < ncols) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(smem + stage_off(row, ch * 16));
+      *reinterpret_cast<uint4 *>(Out + (size_t)(tl.row0 + row) * Nout + n0 + ch * 8) = v;
+    }
+  }
+}
+
 template <bool GATE_UP, int BM, int BK, int NS, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
     const int32_t *__restrict__ off, uint16_t *__restrict__ Out, int E_L, int Kdim,
     int Nout, int n_tiles_n) {
   using P = BigTile<BM, BK, NS, NW>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * P::STAGE_BYTES];
+  // two A stages, NS B stages (NS = 3: the weight rows, which miss to HBM
+  // more often, get two steps to land)
+  static_assert(NS == 2 || NS == 3, "B stages");
+  constexpr int B_BASE = 2 * P::A_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[B_BASE + NS * P::B_BYTES];
 
   const uint32_t smem_l = lds_addr(smem);
   const Tile tl = find_tile<MOE_TILE_NGROUP>(off, E_L, BM, n_tiles_n);
@@ -444,7 +534,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
                              : P::BW / 2 + wn * (P::WTN / 2) + (t - P::TN / 2) * 32;
     else
       brow = wn * P::WTN + t * 32;
-    fb[t] = P::A_BYTES + (brow + fr) * P::ROW_B;
+    fb[t] = (brow + fr) * P::ROW_B;
   }
 
   f32x16_t acc[P::TM][P::TN];
@@ -461,38 +551,39 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
   const int nvalid = min(BM, tl.row_end - tl.row0);
   const int vt = __builtin_amdgcn_readfirstlane(min(P::TM, max(0, (nvalid - wm * 128 + 31) / 32)));
   uint32_t a_skip = 0;
-  // (with more than two stages the vmcnt waits count a fixed number of loads
-  // per step, so no load is skipped)
 #pragma unroll
   for (int i = 0; i < P::NA; ++i)
-    if (NS == 2 && (wv * P::NA + i) * P::RPI >= ((nvalid + 31) / 32) * 32) a_skip |= 1u << i;
+    if ((wv * P::NA + i) * P::RPI >= ((nvalid + 31) / 32) * 32) a_skip |= 1u << i;
   a_skip = __builtin_amdgcn_readfirstlane(a_skip);
-  // prologue: K steps 0 .. NS-2 into stages 0 .. NS-2
+  // prologue: A step 0, B steps 0 .. NS-2 (in this order: the waits below
+  // rely on every A load of a step being issued before that step's B loads)
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < nk)
-      big_issue<BM, BK, NS, NW>(A, Wj, a_off, b_off, s * BK, wv,
-                                smem_l + s * P::STAGE_BYTES);
+    big_issue<BM, BK, NS, NW>(A, Wj, a_off, b_off, 0, min(s, nk - 1) * BK, wv, smem_l,
+                              smem_l + B_BASE + s * P::B_BYTES, s == 0);
   // one main loop per count of valid 32-row tiles of this wave (TM for full
   // tiles; fewer on an expert's last m-tile), each with a single inlined step
   bf16x8_t fra[2][P::TM], frb[2][P::TN];
   auto main_loop = [&](auto vt_tag) {
     constexpr int VT = decltype(vt_tag)::value;
     for (int kb = 0; kb < nk; ++kb) {
-      // this wave's loads of step kb have landed once at most the loads of
-      // steps kb+1 .. kb+NS-2 are still in flight; then every wave's have
-      if (kb + NS - 2 <= nk - 1) wait_vmcnt<(NS - 2) * P::L>();
-      else wait_vmcnt<0>();
+      // step j issues A(j+1) then B(j+NS-1): A(kb) and B(kb) have landed once
+      // at most the NS-2 younger B steps' loads are in flight; after the
+      // barrier, every wave's have
+      wait_vmcnt<(NS - 2) * P::NB>();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      const int ls = (kb + NS - 1) % NS;   // stage read in step kb-1: free after the barrier
-      const uint32_t ldl = smem_l + ls * P::STAGE_BYTES;
-      const uint8_t *rd = smem + (kb % NS) * P::STAGE_BYTES;
-      // the last NS-1 steps reload the last K step into stages no longer
-      // read, so every step issues the same loads (no branch around them)
-      big_step<GATE_UP, BM, BK, NS, NW, VT>(A, Wj, a_off, b_off, min(kb + NS - 1, nk - 1) * BK,
-                                            wv, ldl, rd, fa, fb, khalf, sw, acc, fra, frb, a_skip);
+      // stages read in step kb-1 are free after the barrier; the last steps
+      // reload the last K step into free stages, so every step issues the
+      // same loads (no branch around them)
+      const uint32_t lda = smem_l + ((kb + 1) & 1) * P::A_BYTES;
+      const uint32_t ldb = smem_l + B_BASE + ((kb + NS - 1) % NS) * P::B_BYTES;
+      const uint8_t *rda = smem + (kb & 1) * P::A_BYTES;
+      const uint8_t *rdb = smem + B_BASE + (kb % NS) * P::B_BYTES;
+      big_step<GATE_UP, BM, BK, NS, NW, VT>(A, Wj, a_off, b_off, min(kb + 1, nk - 1) * BK,
+                                            min(kb + NS - 1, nk - 1) * BK, wv, lda, ldb, rda,
+                                            rdb, fa, fb, khalf, sw, acc, fra, frb, a_skip);
     }
   };
   static_assert(P::TM == 4, "main-loop variants");
@@ -504,70 +595,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
     default: main_loop(std::integral_constant<int, 0>{}); break;
   }
 
-  // Epilogue, staged through LDS so that global stores are whole 16-byte
-  // vectors along output rows (the MFMA result layout gives each lane one
-  // column: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
-  // of its 32x32 tile).
-  //  1. neighbouring lanes swap one value (DPP quad permute 1,0,3,2) so each
-  //     lane holds two adjacent columns of one row and writes them as one
-  //     bf16x2 dword into a row-major LDS tile;
-  //  2. every thread copies 16-byte chunks of the tile to global memory,
-  //     skipping rows past the expert's last valid row and columns past Nout.
-  // LDS rows are OUTC bf16; 16-byte chunk c of row r sits at c ^ (4 * q(r))
-  // with q(r) = bit0(r) | bit2(r) << 1, so the four rows one dword write
-  // instruction touches (R, R+1, R+4, R+5) land in four distinct 64-byte
-  // bank groups.
-  constexpr int OUTC = GATE_UP ? P::BW / 2 : P::BW;    // output columns per block
-  constexpr int ROWB = OUTC * 2;                       // bytes per staged row
-  static_assert(BM * ROWB <= NS * P::STAGE_BYTES, "epilogue tile fits the stages");
   wait_vmcnt<0>();   // no direct load still in flight into the stages
   __syncthreads();   // every wave is done reading the last stage
-  auto stage_off = [](int row, int colb) {   // byte offset of (row, byte column)
-    const int q = (row & 1) | (((row >> 2) & 1) << 1);
-    return row * ROWB + ((((colb >> 4) ^ (q << 2))) << 4) + (colb & 15);
-  };
-  const bool odd = (lane & 1) != 0;
-#pragma unroll
-  for (int tm = 0; tm < P::TM; ++tm) {
-#pragma unroll
-    for (int tn = 0; tn < (GATE_UP ? P::TN / 2 : P::TN); ++tn) {
-      const int colb0 = (GATE_UP ? wn * (P::WTN / 2) : wn * P::WTN) * 2 + tn * 64;  // tile col * 2
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float v0, v1;
-        if (GATE_UP) {
-          const float g0 = acc[tm][tn][r], u0 = acc[tm][tn + P::TN / 2][r];
-          const float g1 = acc[tm][tn][r + 1], u1 = acc[tm][tn + P::TN / 2][r + 1];
-          v0 = g0 * __builtin_amdgcn_rcpf(1.0f + __expf(-g0)) * u0;
-          v1 = g1 * __builtin_amdgcn_rcpf(1.0f + __expf(-g1)) * u1;
-        } else {
-          v0 = acc[tm][tn][r];
-          v1 = acc[tm][tn][r + 1];
-        }
-        // even lane keeps row r and takes its partner's row-r value; odd
-        // lane keeps row r+1 and takes its partner's row-(r+1) value
-        const float send = odd ? v0 : v1;
-        const float recv = __int_as_float(
-            __builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
-        const int row = wm * 128 + tm * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3) + (odd ? 1 : 0);
-        const int colb = colb0 + (fr & ~1) * 2;
-        const uint32_t packed = odd ? pack_bf16x2(recv, v1) : pack_bf16x2(v0, recv);
-        *reinterpret_cast<uint32_t *>(smem + stage_off(row, colb)) = packed;
-      }
-    }
-  }
-  __syncthreads();
-  constexpr int CPR = ROWB / 16;                        // 16-byte chunks per row
-  const int ncols = min(OUTC, Nout - n0);               // multiple of 8
-  const int nrows = min(BM, tl.row_end - tl.row0);
-#pragma unroll 4
-  for (int idx = tid; idx < BM * CPR; idx += 64 * NW) {
-    const int row = idx / CPR, ch = idx % CPR;
-    if (row < nrows && ch * 8 < ncols) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(smem + stage_off(row, ch * 16));
-      *reinterpret_cast<uint4 *>(Out + (size_t)(tl.row0 + row) * Nout + n0 + ch * 8) = v;
-    }
-  }
+  big_epilogue<GATE_UP, BM, NW>(acc, smem, tl, Out, Nout, n0, wm, wn);
 }
 
 // ------------------------------------------------------------------ fp32 SIMT
@@ -660,7 +690,7 @@ int launch_bf16(const moe_shape_t &s, const uint16_t *A, const uint16_t *W, cons
   if (Kdim % 64 == 0) {
     constexpr int BM = 256;
     const int ntn = (int)ceil_div(Nout, GATE_UP ? 128 : 256);
-    hipLaunchKernelGGL((k_gemm_bf16_big<GATE_UP, BM, 64, 2, MOE_GEMM_WAVES>),
+    hipLaunchKernelGGL((k_gemm_bf16_big<GATE_UP, BM, 64, MOE_BSTAGES, MOE_GEMM_WAVES>),
                        dim3(grid_blocks(s, BM, ntn)), dim3(64 * MOE_GEMM_WAVES), 0, st, A, W, off,
                        Out, E_L, Kdim, Nout, ntn);
   } else {
