@@ -305,24 +305,6 @@ __device__ __forceinline__ void big_issue(const uint16_t *__restrict__ A,
   for (int i = 0; i < P::NB; ++i) dma16(Wj + b_off[i] + kb, sb + (wv * P::NB + i) * 1024);
 }
 
-// Order in which a sub-step's fragments are read: the order of their first
-// use by the MFMA sequence (A0 B0 B1 A1 A2 A3 for 4 x 2 tiles), so that the
-// MFMAs at the start of a sub-step wait only for the oldest reads.
-template <int TM, int TN>
-struct FragOrder {
-  int q[TM + TN];
-  constexpr FragOrder() : q() {
-    bool seen[TM + TN] = {};
-    int n = 0;
-    for (int m = 0; m < TM * TN; ++m) {
-      const int a = m / TN, b = TM + m % TN;
-      if (!seen[a]) { seen[a] = true; q[n++] = a; }
-      if (!seen[b]) { seen[b] = true; q[n++] = b; }
-    }
-  }
-};
-
-
 // One main-loop step: run the MFMAs of this K step from `rd` while issuing
 // the direct loads of a later K step into `ld`. The stages are restrict
 // pointers so that, once inlined, the compiler does not wait for the loads

@@ -50,6 +50,23 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Order in which a sub-step's fragments are read: the order of their first
+// use by the MFMA sequence (A0 B0 B1 A1 A2 A3 for 4 x 2 tiles), so that the
+// MFMAs at the start of a sub-step wait only for the oldest reads.
+template <int TM, int TN>
+struct FragOrder {
+  int q[TM + TN];
+  constexpr FragOrder() : q() {
+    bool seen[TM + TN] = {};
+    int n = 0;
+    for (int m = 0; m < TM * TN; ++m) {
+      const int a = m / TN, b = TM + m % TN;
+      if (!seen[a]) { seen[a] = true; q[n++] = a; }
+      if (!seen[b]) { seen[b] = true; q[n++] = b; }
+    }
+  }
+};
+
 // Row-grouped GEMM tiles from the device offsets of the local experts: the
 // grid is sized from the capacity bound, every block recomputes the
 // per-expert m-tile counts (tm rows each) with a wave scan and maps itself to
