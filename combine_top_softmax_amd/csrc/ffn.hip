@@ -362,8 +362,8 @@ __device__ __forceinline__ void big_step(
   auto mfma = [&](int buf, int q) {
     const int i = q / P::TN, j = q % P::TN;
     if (i < VT)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fra[buf][i], frb[buf][j], acc[i][j],
-                                                          0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frb[buf][j], fra[buf][i], acc[i][j],
+                                                          0, 0, 0);   // transposed tile
   };
 #pragma unroll
   for (int r = 0; r < P::TM + P::TN; ++r) read_frag(0, 0, r);
@@ -391,65 +391,60 @@ __device__ __forceinline__ void big_epilogue(
     int wm, int wn) {
   using P = BigTile<BM, 64, 2, NW>;
   // Epilogue, staged through LDS so that global stores are whole 16-byte
-  // vectors along output rows (the MFMA result layout gives each lane one
-  // column: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
-  // of its 32x32 tile).
-  //  1. neighbouring lanes swap one value (DPP quad permute 1,0,3,2) so each
-  //     lane holds two adjacent columns of one row and writes them as one
-  //     bf16x2 dword into a row-major LDS tile;
-  //  2. every thread copies 16-byte chunks of the tile to global memory,
-  //     skipping rows past the expert's last valid row and columns past Nout.
-  // LDS rows are OUTC bf16; 16-byte chunk c of row r sits at c ^ (4 * q(r))
-  // with q(r) = bit0(r) | bit2(r) << 1, so the four rows one dword write
-  // instruction touches (R, R+1, R+4, R+5) land in four distinct 64-byte
-  // bank groups.
+  // vectors along output rows. The MFMAs take the weight fragment as their
+  // first operand, so each 32x32 accumulator tile holds the transposed tile:
+  // register r of lane l is row l%32, column 8*(r/4) + 4*(l/32) + r%4 of the
+  // output tile, i.e. every lane owns four runs of four adjacent columns of
+  // one row. Each run is converted to four bf16 (two packed conversions) and
+  // written as one 8-byte LDS store; then every thread copies 16-byte chunks
+  // of the tile to global memory, skipping rows past the expert's last valid
+  // row and columns past Nout.
+  // LDS rows are OUTC bf16; 16-byte chunk c of row r sits at c ^ (r % CPR)
+  // (CPR chunks per row), so the 16 consecutive rows that one 16-lane group
+  // of a store instruction writes land in 16 distinct chunks.
   constexpr int OUTC = GATE_UP ? P::BW / 2 : P::BW;    // output columns per block
   constexpr int ROWB = OUTC * 2;                       // bytes per staged row
+  constexpr int CPR = ROWB / 16;                       // 16-byte chunks per row
   static_assert(BM * ROWB <= 2 * P::A_BYTES + 2 * P::B_BYTES, "epilogue tile fits the stages");
   const int tid = threadIdx.x, lane = tid & 63, fr = lane & 31, khalf = lane >> 5;
-  auto stage_off = [](int row, int colb) {   // byte offset of (row, byte column)
-    const int q = (row & 1) | (((row >> 2) & 1) << 1);
-    return row * ROWB + ((((colb >> 4) ^ (q << 2))) << 4) + (colb & 15);
+  auto stage_off = [](int row, int chunk) {   // byte offset of 16-byte chunk `chunk` of `row`
+    return row * ROWB + ((chunk ^ (row & (CPR - 1))) << 4);
   };
-  const bool odd = (lane & 1) != 0;
 #pragma unroll
   for (int tm = 0; tm < P::TM; ++tm) {
+    const int row = wm * 128 + tm * 32 + fr;
 #pragma unroll
     for (int tn = 0; tn < (GATE_UP ? P::TN / 2 : P::TN); ++tn) {
-      const int colb0 = (GATE_UP ? wn * (P::WTN / 2) : wn * P::WTN) * 2 + tn * 64;  // tile col * 2
+      const int col0 = (GATE_UP ? wn * (P::WTN / 2) : wn * P::WTN) + tn * 32;  // tile column
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float v0, v1;
-        if (GATE_UP) {
-          const float g0 = acc[tm][tn][r], u0 = acc[tm][tn + P::TN / 2][r];
-          const float g1 = acc[tm][tn][r + 1], u1 = acc[tm][tn + P::TN / 2][r + 1];
-          v0 = g0 * __builtin_amdgcn_rcpf(1.0f + __expf(-g0)) * u0;
-          v1 = g1 * __builtin_amdgcn_rcpf(1.0f + __expf(-g1)) * u1;
-        } else {
-          v0 = acc[tm][tn][r];
-          v1 = acc[tm][tn][r + 1];
+      for (int g = 0; g < 4; ++g) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          if (GATE_UP) {
+            const float gv = acc[tm][tn][r], uv = acc[tm][tn + P::TN / 2][r];
+            v[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+          } else {
+            v[e] = acc[tm][tn][r];
+          }
         }
-        // even lane keeps row r and takes its partner's row-r value; odd
-        // lane keeps row r+1 and takes its partner's row-(r+1) value
-        const float send = odd ? v0 : v1;
-        const float recv = __int_as_float(
-            __builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
-        const int row = wm * 128 + tm * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3) + (odd ? 1 : 0);
-        const int colb = colb0 + (fr & ~1) * 2;
-        const uint32_t packed = odd ? pack_bf16x2(recv, v1) : pack_bf16x2(v0, recv);
-        *reinterpret_cast<uint32_t *>(smem + stage_off(row, colb)) = packed;
+        const int cb = (col0 + 8 * g + 4 * khalf) * 2;   // byte column of the run
+        uint2 w;
+        w.x = pack2_bf16(v[0], v[1]);
+        w.y = pack2_bf16(v[2], v[3]);
+        *reinterpret_cast<uint2 *>(smem + stage_off(row, cb >> 4) + (cb & 15)) = w;
       }
     }
   }
   __syncthreads();
-  constexpr int CPR = ROWB / 16;                        // 16-byte chunks per row
   const int ncols = min(OUTC, Nout - n0);               // multiple of 8
   const int nrows = min(BM, tl.row_end - tl.row0);
 #pragma unroll 4
   for (int idx = tid; idx < BM * CPR; idx += 64 * NW) {
     const int row = idx / CPR, ch = idx % CPR;
     if (row < nrows && ch * 8 < ncols) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(smem + stage_off(row, ch * 16));
+      const uint4 v = *reinterpret_cast<const uint4 *>(smem + stage_off(row, ch));
       *reinterpret_cast<uint4 *>(Out + (size_t)(tl.row0 + row) * Nout + n0 + ch * 8) = v;
     }
   }

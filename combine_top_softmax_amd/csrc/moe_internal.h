@@ -78,6 +78,13 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
 }
+// Same result as pack_bf16x2 (round to nearest even) in one packed conversion.
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 
 // Wave-wide inclusive prefix sum of an int (64 lanes).
 __device__ __forceinline__ int wave_incl_scan(int v) {
