@@ -50,58 +50,26 @@ struct Tile {
   bool valid;
 };
 
-// Map this block to a (expert, m-tile, n-tile) from the local offsets.
-// Executed redundantly by every wave of the block; the result is wave-uniform.
-// Tiles are numbered expert by expert; inside an expert with M m-tiles and
-// n_tiles_n n-tiles, they go in groups of NG n-tiles: all M m-tiles of the
-// first NG n-tiles, then the next group, so the tiles that run at the same
-// time on one XCD share both their A rows and their weight panels in L2.
+// Map this block to a (expert, m-tile, n-tile) from the local offsets (the
+// shared lookup above; wave-uniform). Inside an expert with M m-tiles, tiles
+// go in groups of NG n-tiles: all M m-tiles of the first NG n-tiles, then the
+// next group, so the tiles that run at the same time on one XCD share both
+// their A rows and their weight panels in L2.
 template <int NG>
 __device__ __forceinline__ Tile find_tile(const int32_t *__restrict__ off, int E_L, int bm,
                                           int n_tiles_n) {
-  const int lane = threadIdx.x & 63;
   Tile tl;
-  tl.valid = false;
-  int total_m = 0;
-  for (int c = 0; c < E_L; c += 64) {
-    const int j = c + lane;
-    const int n = (j < E_L) ? off[j + 1] - off[j] : 0;
-    const int incl = wave_incl_scan((n + bm - 1) / bm);
-    total_m += __shfl(incl, 63, 64);
-  }
-  const int total = total_m * n_tiles_n;
-  const int q = (total + kNumXcd - 1) / kNumXcd;
-  const int b = blockIdx.x;
-  const int slot = b / kNumXcd;
-  const int L = (b % kNumXcd) * q + slot;
-  if (slot >= q || L >= total) return tl;
-  const int m_glob = L / n_tiles_n;      // which expert: the one holding m-tile m_glob
-  int run = 0;
-  for (int c = 0; c < E_L; c += 64) {
-    const int j = c + lane;
-    const int n = (j < E_L) ? off[j + 1] - off[j] : 0;
-    const int mt = (n + bm - 1) / bm;
-    const int incl = wave_incl_scan(mt);
-    const int tot = __shfl(incl, 63, 64);
-    if (m_glob < run + tot) {
-      const uint64_t hit = __ballot(m_glob < run + incl);
-      const int first = __builtin_ctzll(hit);
-      const int mstart = run + __shfl(incl - mt, first, 64);   // first m-tile of the expert
-      const int M = __shfl(mt, first, 64);
-      const int e = c + first;
-      const int li = L - mstart * n_tiles_n;                   // tile index inside the expert
-      const int g = li / (M * NG);                             // n-group
-      const int w = min(NG, n_tiles_n - g * NG);               // n-tiles in this group
-      const int r = li - g * NG * M;
-      tl.expert = e;
-      tl.row0 = off[e] + (r / w) * bm;
-      tl.row_end = off[e + 1];
-      tl.n_idx = g * NG + r % w;
-      tl.valid = true;
-      return tl;
-    }
-    run += tot;
-  }
+  const ExpertTile x = find_expert_tile(off, E_L, bm, n_tiles_n);
+  tl.valid = x.valid;
+  if (!x.valid) return tl;
+  const int li = x.L - x.mstart * n_tiles_n;   // tile index inside the expert, < M * n_tiles_n
+  const int g = li / (x.M * NG);               // n-group
+  const int w = min(NG, n_tiles_n - g * NG);   // n-tiles in this group
+  const int r = li - g * NG * x.M;
+  tl.expert = x.e;
+  tl.row0 = x.row_begin + (r / w) * bm;
+  tl.row_end = x.row_end;
+  tl.n_idx = g * NG + r % w;
   return tl;
 }
 

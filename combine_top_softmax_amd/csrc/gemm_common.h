@@ -67,12 +67,101 @@ struct FragOrder {
   }
 };
 
-// Row-grouped GEMM tiles from the device offsets of the local experts: the
-// grid is sized from the capacity bound, every block recomputes the
-// per-expert m-tile counts (tm rows each) with a wave scan and maps itself to
-// (expert, m-tile, n-tile) or exits. XCD-aware order: blocks are dealt to the
-// 8 XCDs round-robin, so block b takes tile (b % 8) * q + b / 8 and each XCD
-// walks a contiguous run of tiles. Wave-uniform result.
+// Wave-wide inclusive prefix sum over the 64 lanes in DPP moves (no LDS round
+// trip): shifts by 1, 2, 4 and 8 lanes inside each row of 16 lanes (lanes
+// with no source add 0), then lane 15 of rows 0 and 2 added into rows 1 and 3,
+// then lane 31 added into the upper half. All 64 lanes must be active.
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+
+// 64 local experts as the lanes of a wave hold them: lane j has expert c + j's
+// buffer rows [o0, o1), its count of bm-row m-tiles and the inclusive scan of
+// those counts over the chunk; tot is the chunk's total (wave-uniform).
+struct ExpertChunk {
+  int o0, o1, mt, incl, tot;
+};
+
+__device__ __forceinline__ ExpertChunk expert_chunk(const int32_t *__restrict__ off, int E_L, int c,
+                                                    int bm) {
+  const int j = c + (threadIdx.x & 63);
+  ExpertChunk ch;
+  ch.o0 = 0;
+  ch.o1 = 0;
+  if (j < E_L) {
+    ch.o0 = off[j];
+    ch.o1 = off[j + 1];
+  }
+  ch.mt = (max(ch.o1 - ch.o0, 0) + bm - 1) / bm;
+  ch.incl = wave_incl_scan_dpp(ch.mt);
+  ch.tot = __builtin_amdgcn_readlane(ch.incl, 63);
+  return ch;
+}
+
+// Grouped GEMM tiles from the device offsets of the local experts: the grid is
+// sized from the capacity bound, every block counts the experts' m-tiles (bm
+// rows each) and maps itself to tile L of the XCD-aware order, or exits.
+// Blocks are dealt to the 8 XCDs round-robin, so block b takes tile
+// (b % 8) * q + b / 8 and each XCD walks a contiguous run of tiles; tiles are
+// numbered expert by expert (n_tiles_n per m-tile). The offsets are read once
+// (one load per lane for up to 64 experts) and everything after is register
+// work. The result is wave-uniform and, whatever the scan returns, names an
+// expert below E_L with at least one row and an m-tile inside it, so every
+// address the kernels form from it stays inside that expert's rows.
+struct ExpertTile {
+  int L;          // this block's tile index
+  int e;          // expert
+  int mstart;     // index of the expert's first m-tile among all m-tiles
+  int M;          // m-tiles of the expert
+  int row_begin;  // the expert's buffer rows [row_begin, row_end)
+  int row_end;
+  bool valid;
+};
+
+__device__ __forceinline__ ExpertTile find_expert_tile(const int32_t *__restrict__ off, int E_L,
+                                                       int bm, int n_tiles_n) {
+  ExpertTile t;
+  t.valid = false;
+  const ExpertChunk c0 = expert_chunk(off, E_L, 0, bm);
+  int total_m = c0.tot;
+  for (int c = 64; c < E_L; c += 64) total_m += expert_chunk(off, E_L, c, bm).tot;
+  const int total = total_m * n_tiles_n;
+  const int q = (total + kNumXcd - 1) / kNumXcd;
+  const int slot = blockIdx.x / kNumXcd;
+  const int L = (blockIdx.x % kNumXcd) * q + slot;
+  if (slot >= q || L >= total) return t;
+  const int m_glob = L / n_tiles_n;
+  int run = 0;
+  for (int c = 0; c < E_L; c += 64) {
+    const ExpertChunk ch = (c == 0) ? c0 : expert_chunk(off, E_L, c, bm);
+    if (m_glob < run + ch.tot) {
+      const uint64_t hit = __ballot(m_glob < run + ch.incl);
+      if (hit == 0) return t;
+      const int first = __builtin_ctzll(hit);
+      const int M = __builtin_amdgcn_readlane(ch.mt, first);
+      const int mstart = run + __builtin_amdgcn_readlane(ch.incl, first) - M;
+      if (c + first >= E_L || M <= 0 || m_glob < mstart || m_glob >= mstart + M) return t;
+      t.L = L;
+      t.e = c + first;
+      t.M = M;
+      t.mstart = mstart;
+      t.row_begin = __builtin_amdgcn_readlane(ch.o0, first);
+      t.row_end = __builtin_amdgcn_readlane(ch.o1, first);
+      t.valid = true;
+      return t;
+    }
+    run += ch.tot;
+  }
+  return t;
+}
+
+// Row-mode tiles: m-tile by m-tile, its n_tiles_n n-tiles consecutive.
 struct RowTile {
   int expert, row0, row_end, n_idx;
   bool valid;
@@ -80,44 +169,15 @@ struct RowTile {
 
 __device__ __forceinline__ RowTile find_row_tile(const int32_t *__restrict__ off, int E_L, int tm,
                                                  int n_tiles_n) {
-  const int lane = threadIdx.x & 63;
   RowTile tl;
-  tl.valid = false;
-  int total_m = 0;
-  for (int c = 0; c < E_L; c += 64) {
-    const int j = c + lane;
-    const int n = (j < E_L) ? off[j + 1] - off[j] : 0;
-    const int incl = wave_incl_scan((n + tm - 1) / tm);
-    total_m += __shfl(incl, 63, 64);
-  }
-  const int total = total_m * n_tiles_n;
-  const int q = (total + kNumXcd - 1) / kNumXcd;
-  const int b = blockIdx.x;
-  const int slot = b / kNumXcd;
-  const int L = (b % kNumXcd) * q + slot;
-  if (slot >= q || L >= total) return tl;
-  const int m_glob = L / n_tiles_n;
-  tl.n_idx = L - m_glob * n_tiles_n;
-  int run = 0;
-  for (int c = 0; c < E_L; c += 64) {
-    const int j = c + lane;
-    const int n = (j < E_L) ? off[j + 1] - off[j] : 0;
-    const int mt = (n + tm - 1) / tm;
-    const int incl = wave_incl_scan(mt);
-    const int tot = __shfl(incl, 63, 64);
-    if (m_glob < run + tot) {
-      const uint64_t hit = __ballot(m_glob < run + incl);
-      const int first = __builtin_ctzll(hit);
-      const int excl = __shfl(incl - mt, first, 64);
-      const int e = c + first;
-      tl.expert = e;
-      tl.row0 = off[e] + (m_glob - run - excl) * tm;
-      tl.row_end = off[e + 1];
-      tl.valid = true;
-      return tl;
-    }
-    run += tot;
-  }
+  const ExpertTile x = find_expert_tile(off, E_L, tm, n_tiles_n);
+  tl.valid = x.valid;
+  if (!x.valid) return tl;
+  const int m_glob = x.L / n_tiles_n;
+  tl.expert = x.e;
+  tl.row0 = x.row_begin + (m_glob - x.mstart) * tm;
+  tl.row_end = x.row_end;
+  tl.n_idx = x.L - m_glob * n_tiles_n;
   return tl;
 }
 
