@@ -67,20 +67,6 @@ struct FragOrder {
   }
 };
 
-// Wave-wide inclusive prefix sum over the 64 lanes in DPP moves (no LDS round
-// trip): shifts by 1, 2, 4 and 8 lanes inside each row of 16 lanes (lanes
-// with no source add 0), then lane 15 of rows 0 and 2 added into rows 1 and 3,
-// then lane 31 added into the upper half. All 64 lanes must be active.
-__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
-  return v;
-}
-
 // 64 local experts as the lanes of a wave hold them: lane j has expert c + j's
 // buffer rows [o0, o1), its count of bm-row m-tiles and the inclusive scan of
 // those counts over the chunk; tot is the chunk's total (wave-uniform).

@@ -11,7 +11,7 @@
 namespace moe {
 
 constexpr int kWave = 64;          // CDNA wavefront width
-constexpr int kRouteTile = 64;     // tokens per routing tile (one wave, one lane per token)
+constexpr int kRouteTile = 64;     // tokens per routing tile (one lane per token in its ballots)
 constexpr int kNumXcd = 8;         // MI355X: 8 accelerator complex dies, each with its own L2
 
 // ---- host-side helpers -----------------------------------------------------
@@ -86,15 +86,19 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// Wave-wide inclusive prefix sum of an int (64 lanes).
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int n = __shfl_up(v, o, kWave);
-    if (lane >= o) v += n;
-  }
+// Wave-wide inclusive prefix sum over the 64 lanes in DPP moves (no LDS round
+// trip): shifts by 1, 2, 4 and 8 lanes inside each row of 16 lanes (lanes
+// with no source add 0), then lane 15 of rows 0 and 2 added into rows 1 and 3,
+// then lane 31 added into the upper half. All 64 lanes must be active.
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
   return v;
 }
+
 
 }  // namespace moe

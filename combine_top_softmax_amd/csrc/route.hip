@@ -11,10 +11,12 @@
 //   p = (routes to e in earlier 64-token tiles) + (earlier lanes of this tile
 //       that route to e).
 // Three kernels compute it without atomics and without a host round trip:
-//   k_route_tile   one wave per 64-token tile (one lane per token): top-K in
-//                  registers, fp64 softmax over the K winners, then per expert
-//                  a wave ballot of "my token routes to e"; the ballot masks go
-//                  to LDS, popcount(mask) is the tile histogram and
+//   k_route_tile   one 4-wave block per 64-token tile: top-K selection with
+//                  one DPP quad of 4 lanes per token (sorted 64-bit keys per
+//                  lane, K rounds of a quad-wide max), fp64 softmax over the K
+//                  winners, then per expert a wave ballot of "my token routes
+//                  to e" (lane = token); the ballot masks go to LDS,
+//                  popcount(mask) is the tile histogram and
 //                  popcount(mask & lanes-below) the in-tile rank.
 //   k_tile_scan    one block per expert: exclusive scan of its tile histogram
 //                  column -> tile bases; the total is counts[e].
@@ -30,82 +32,196 @@
 namespace moe {
 namespace {
 
-// Insert (x, i) into a list sorted by (value desc, index asc); the smallest
-// element falls off the end. Elements arrive in ascending index, so a strict
-// '>' keeps the earlier (lower) id ahead on ties; IEEE '>' treats -0.0 and +0.0
-// as equal. Once the new element has been placed, every later slot shifts.
+constexpr int kRouteWaves = 4;    // waves per 64-token routing tile
+constexpr int kTokLanes = 4;      // lanes per token while selecting (one DPP quad)
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Sort key of (logit x, expert id) for the order "logit descending, id
+// ascending" that a stable sort of -logit gives: IEEE comparison, so -0.0 and
+// +0.0 are one value; -inf is the smallest number; NaN after every number,
+// NaNs in id order. High word: the value's rank (0 for NaN); low word: ~id.
+// Key 0 is an empty slot. Keys of distinct ids are distinct.
+__device__ __forceinline__ uint64_t route_key(float x, int id) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;                            // -0.0 -> +0.0
+  uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  if ((u & 0x7fffffffu) > 0x7f800000u) hi = 0u;             // NaN
+  return ((uint64_t)hi << 32) | (uint32_t)~(uint32_t)id;
+}
+
+__device__ __forceinline__ float route_key_value(uint64_t key) {
+  const uint32_t hi = (uint32_t)(key >> 32);
+  if (hi == 0u) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
+}
+
+__device__ __forceinline__ int route_key_id(uint64_t key) {
+  return key == 0 ? -1 : (int)~(uint32_t)key;
+}
+
+// Insert x into k[] kept in descending order; the smallest key falls off.
 template <int KM>
-__device__ __forceinline__ void topk_insert(float (&v)[KM], int (&ix)[KM], float x, int i) {
-  bool placed = false;
+__device__ __forceinline__ void key_insert(uint64_t (&k)[KM], uint64_t x) {
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
-    const bool sw = placed || (x > v[j]);
-    const float tv = v[j];
-    const int ti = ix[j];
-    v[j] = sw ? x : tv;
-    ix[j] = sw ? i : ti;
-    x = sw ? tv : x;
-    i = sw ? ti : i;
-    placed = sw;
+    const uint64_t a = k[j];
+    const bool sw = x > a;
+    k[j] = sw ? x : a;
+    x = sw ? a : x;
   }
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf,
+                                                            false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL,
+                                                            0xf, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Largest key over the 4 lanes of each quad (quad_perm [1,0,3,2], [2,3,0,1]).
+__device__ __forceinline__ uint64_t quad_max_key(uint64_t v) {
+  uint64_t o = dpp_u64<0xb1>(v);
+  v = o > v ? o : v;
+  o = dpp_u64<0x4e>(v);
+  return o > v ? o : v;
+}
+
+// Quad lane L's value, in every lane of the quad (quad_perm [L,L,L,L]).
+template <int L>
+__device__ __forceinline__ double quad_bcast(double v) {
+  return __builtin_bit_cast(double, dpp_u64<L * 0x55>(__builtin_bit_cast(uint64_t, v)));
+}
+
+// Route tile: 64 tokens, 4 waves. Selection (from logits): wave w takes
+// tokens 16w .. 16w+15, one DPP quad of 4 lanes each; lane s of a quad keeps
+// the sorted top keys of logits 4s..4s+3 (+ 16 r), then K rounds take the
+// quad's largest head key (the lane that held it drops it), so every lane of
+// the quad sees the K winners in order; lane s owns slots s, s+4, s+8, s+12.
+// Softmax: each owner forms exp(l_j - m) in fp64, every lane of the quad sums
+// the K terms in slot order (quad broadcasts), weights rounded once to fp32.
+// Ballots (lane = token): wave w builds the masks of experts 16w .. 16w+15 of
+// each 64-expert chunk; ranks: wave w takes the slots j with j % 4 == w.
 template <int KM, bool FROM_LOGITS>
-__global__ __launch_bounds__(64) void k_route_tile(
+__global__ __launch_bounds__(64 * kRouteWaves) void k_route_tile(
     const float *__restrict__ logits, const int32_t *__restrict__ ids_in,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
     int32_t *__restrict__ hist, uint8_t *__restrict__ rank_ws,
     int T, int N, int K, int ntiles) {
+  constexpr int TPW = kWave / kTokLanes;                 // tokens per wave
+  constexpr int SPL = (KM + kTokLanes - 1) / kTokLanes;  // slots per lane
+  static_assert(kRouteTile == TPW * kRouteWaves, "route tile layout");
   __shared__ uint64_t s_mask[MOE_MAX_EXPERTS];
-  const int lane = threadIdx.x;
+  __shared__ int32_t s_ix[KM * kRouteTile];   // slot-major: s_ix[j * 64 + token]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = blockIdx.x;
-  const int t = tile * kRouteTile + lane;
-  const bool active = t < T;
+  const int t0 = tile * kRouteTile;
 
-  int ix[KM];
   if constexpr (FROM_LOGITS) {
-    float v[KM];
+    const int s = lane & (kTokLanes - 1);
+    const int tt = TPW * wv + lane / kTokLanes;   // token within the tile
+    const int t = t0 + tt;
+    uint64_t key[KM];
 #pragma unroll
-    for (int j = 0; j < KM; ++j) { v[j] = -INFINITY; ix[j] = -1; }
-    if (active) {
+    for (int j = 0; j < KM; ++j) key[j] = 0;
+    if (t < T) {
       const float *row = logits + (size_t)t * N;
       if ((N & 3) == 0) {
-        typedef float f32x4_t __attribute__((ext_vector_type(4)));
-        const f32x4_t *row4 = reinterpret_cast<const f32x4_t *>(row);
-        for (int q = 0; q < (N >> 2); ++q) {
-          const f32x4_t f = __builtin_nontemporal_load(row4 + q);
-          topk_insert<KM>(v, ix, f.x, 4 * q + 0);
-          topk_insert<KM>(v, ix, f.y, 4 * q + 1);
-          topk_insert<KM>(v, ix, f.z, 4 * q + 2);
-          topk_insert<KM>(v, ix, f.w, 4 * q + 3);
+        // up to 4 vector loads in flight per lane (all of a 64-expert row)
+        constexpr int LPI = 4;
+        for (int b0 = 4 * s; b0 < N; b0 += 4 * kTokLanes * LPI) {
+          f32x4_t f[LPI];
+#pragma unroll
+          for (int u = 0; u < LPI; ++u) {
+            const int e0 = b0 + 4 * kTokLanes * u;
+            if (e0 < N)
+              f[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(row + e0));
+          }
+#pragma unroll
+          for (int u = 0; u < LPI; ++u) {
+            const int e0 = b0 + 4 * kTokLanes * u;
+            if (e0 < N) {
+              key_insert<KM>(key, route_key(f[u].x, e0 + 0));
+              key_insert<KM>(key, route_key(f[u].y, e0 + 1));
+              key_insert<KM>(key, route_key(f[u].z, e0 + 2));
+              key_insert<KM>(key, route_key(f[u].w, e0 + 3));
+            }
+          }
         }
       } else {
-        for (int e = 0; e < N; ++e) topk_insert<KM>(v, ix, row[e], e);
+        for (int e = s; e < N; e += kTokLanes) key_insert<KM>(key, route_key(row[e], e));
       }
-      // softmax over the K selected logits, in fp64, rounded once to fp32
-      const double m = (double)v[0];
-      double ex[KM];
-      double sum = 0.0;
+    }
+    uint64_t first = 0;   // slot 0's key
+    uint64_t mine[SPL];   // slot s + 4 i's key
 #pragma unroll
-      for (int j = 0; j < KM; ++j) {
-        ex[j] = (j < K) ? exp((double)v[j] - m) : 0.0;
-        sum += ex[j];
-      }
+    for (int i = 0; i < SPL; ++i) mine[i] = 0;
 #pragma unroll
-      for (int j = 0; j < KM; ++j) {
-        if (j < K) {
-          topk_idx[(size_t)t * K + j] = ix[j];
-          topk_w[(size_t)t * K + j] = (float)(ex[j] / sum);
+    for (int j = 0; j < KM; ++j) {
+      if (j < K) {
+        const uint64_t m = quad_max_key(key[0]);
+        if (key[0] == m) {          // this lane held the winner: drop it
+#pragma unroll
+          for (int i = 0; i + 1 < KM; ++i) key[i] = key[i + 1];
+          key[KM - 1] = 0;
         }
+        if (j == 0) first = m;
+        if (s == j % kTokLanes) mine[j / kTokLanes] = m;
+      }
+    }
+    // softmax over the K selected logits, in fp64, rounded once to fp32
+    const double mx = (double)route_key_value(first);
+    double ex[SPL];
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+      ex[i] = (s + kTokLanes * i < K) ? exp((double)route_key_value(mine[i]) - mx) : 0.0;
+    double sum = 0.0;             // ex_0 + ex_1 + ... in slot order
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j < K) {
+        double o;
+        switch (j % kTokLanes) {
+          case 0: o = quad_bcast<0>(ex[j / kTokLanes]); break;
+          case 1: o = quad_bcast<1>(ex[j / kTokLanes]); break;
+          case 2: o = quad_bcast<2>(ex[j / kTokLanes]); break;
+          default: o = quad_bcast<3>(ex[j / kTokLanes]); break;
+        }
+        sum += o;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int j = s + kTokLanes * i;
+      if (j < KM) {
+        const int id = route_key_id(mine[i]);
+        if (j < K && t < T) {
+          topk_idx[(size_t)t * K + j] = id;
+          topk_w[(size_t)t * K + j] = (float)(ex[i] / sum);
+        }
+        s_ix[j * kRouteTile + tt] = (j < K && t < T) ? id : -1;
       }
     }
   } else {
-#pragma unroll
-    for (int j = 0; j < KM; ++j) ix[j] = (active && j < K) ? ids_in[(size_t)t * K + j] : -1;
+    for (int q = tid; q < KM * kRouteTile; q += 64 * kRouteWaves) {
+      const int j = q / kRouteTile, tt = q % kRouteTile, t = t0 + tt;
+      s_ix[q] = (j < K && t < T) ? ids_in[(size_t)t * K + j] : -1;
+    }
   }
+  __syncthreads();
 
-  // Per chunk of 64 experts: a ballot per expert; lane j keeps the mask of
-  // expert (64*chunk + j), stores it to LDS and writes the tile histogram.
+  // lane = token from here on
+  const int t = t0 + lane;
+  int ix[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) ix[j] = s_ix[j * kRouteTile + lane];
+
+  // Per chunk of 64 experts: a ballot per expert; wave w keeps the masks of
+  // experts 16w .. 16w+15 of the chunk (in those lanes), stores them to LDS
+  // and writes the tile histogram.
   const int nchunks = (N + kWave - 1) / kWave;
   for (int c = 0; c < nchunks; ++c) {
     uint64_t mine_bits = 0;  // which experts of this chunk my token routes to
@@ -117,24 +233,25 @@ __global__ __launch_bounds__(64) void k_route_tile(
     }
     uint32_t mlo = 0, mhi = 0;
 #pragma unroll
-    for (int j = 0; j < kWave; ++j) {
+    for (int jj = 0; jj < kWave / kRouteWaves; ++jj) {
+      const int j = wv * (kWave / kRouteWaves) + jj;
       const uint64_t b = __ballot((mine_bits >> j) & 1ull);
       mlo = (lane == j) ? (uint32_t)b : mlo;
       mhi = (lane == j) ? (uint32_t)(b >> 32) : mhi;
     }
     const int e = c * kWave + lane;
-    if (e < N) {
+    if (lane / (kWave / kRouteWaves) == wv && e < N) {
       const uint64_t m = ((uint64_t)mhi << 32) | mlo;
       s_mask[e] = m;
       hist[(size_t)e * ntiles + tile] = __popcll(m);
     }
   }
   __syncthreads();
-  if (active) {
+  if (t < T) {
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
-      if (j < K) {
+      if (j < K && (j % kRouteWaves) == wv) {
         const int e = ix[j];
         const int r = (e >= 0 && e < N) ? __popcll(s_mask[e] & below) : 0;
         rank_ws[(size_t)t * K + j] = (uint8_t)r;
@@ -144,6 +261,10 @@ __global__ __launch_bounds__(64) void k_route_tile(
 }
 
 // Exclusive scan of hist[e][0..ntiles) in place; counts[e] = the column total.
+// Thread i takes a run of `per` consecutive tiles; the first kScanRegs values
+// of the run stay in registers between the read and the write.
+constexpr int kScanRegs = 8;
+
 __global__ __launch_bounds__(256) void k_tile_scan(int32_t *__restrict__ hist,
                                                    int32_t *__restrict__ counts, int ntiles) {
   __shared__ int s_wave[4];
@@ -152,17 +273,30 @@ __global__ __launch_bounds__(256) void k_tile_scan(int32_t *__restrict__ hist,
   const int tid = threadIdx.x;
   const int per = (ntiles + 255) / 256;
   const int beg = tid * per;
+  int v[kScanRegs];
   int local = 0;
-  for (int i = 0; i < per; ++i)
+#pragma unroll
+  for (int i = 0; i < kScanRegs; ++i) {
+    v[i] = (i < per && beg + i < ntiles) ? col[beg + i] : 0;
+    local += v[i];
+  }
+  for (int i = kScanRegs; i < per; ++i)
     if (beg + i < ntiles) local += col[beg + i];
-  const int incl = wave_incl_scan(local);
+  const int incl = wave_incl_scan_dpp(local);
   const int w = tid >> 6, lane = tid & 63;
   if (lane == 63) s_wave[w] = incl;
   __syncthreads();
   int wave_base = 0;
   for (int i = 0; i < w; ++i) wave_base += s_wave[i];
   int run = wave_base + incl - local;
-  for (int i = 0; i < per; ++i) {
+#pragma unroll
+  for (int i = 0; i < kScanRegs; ++i) {
+    if (i < per && beg + i < ntiles) {
+      col[beg + i] = run;
+      run += v[i];
+    }
+  }
+  for (int i = kScanRegs; i < per; ++i) {
     if (beg + i < ntiles) {
       const int h = col[beg + i];
       col[beg + i] = run;
@@ -172,6 +306,7 @@ __global__ __launch_bounds__(256) void k_tile_scan(int32_t *__restrict__ hist,
   if (tid == 255) counts[e] = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
 }
 
+template <int KM>
 __global__ __launch_bounds__(64) void k_assign(
     const int32_t *__restrict__ ids, const int32_t *__restrict__ base,
     const uint8_t *__restrict__ rank_ws, const int32_t *__restrict__ counts,
@@ -182,13 +317,26 @@ __global__ __launch_bounds__(64) void k_assign(
   __shared__ int s_g[MOE_MAX_EXPERTS + 1];  // exclusive scan of min(counts, C)
   const int lane = threadIdx.x;
   const int tile = blockIdx.x;
+  const int t = tile * kRouteTile + lane;
+  // this token's experts and in-tile ranks, loaded ahead of the scan
+  int e[KM];
+  uint8_t rk[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    e[k] = -1;
+    rk[k] = 0;
+    if (k < K && t < T) {
+      e[k] = ids[(size_t)t * K + k];
+      rk[k] = rank_ws[(size_t)t * K + k];
+    }
+  }
   {
     const int per = (N + kWave - 1) / kWave;
     const int beg = lane * per;
     int local = 0;
     for (int i = 0; i < per; ++i)
       if (beg + i < N) local += min(counts[beg + i], C);
-    const int incl = wave_incl_scan(local);
+    const int incl = wave_incl_scan_dpp(local);
     int run = incl - local;
     for (int i = 0; i < per; ++i) {
       if (beg + i < N) {
@@ -198,6 +346,11 @@ __global__ __launch_bounds__(64) void k_assign(
     }
     if (lane == 63) s_g[N] = incl;
   }
+  // position of each route in its expert: tile base + in-tile rank
+  int p[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k)
+    p[k] = (e[k] >= 0 && e[k] < N) ? base[(size_t)e[k] * ntiles + tile] + (int)rk[k] : -1;
   __syncthreads();
   if (tile == 0) {
     const int n_off = ep_size * (E_L + 1);
@@ -206,19 +359,18 @@ __global__ __launch_bounds__(64) void k_assign(
       offsets[i] = s_g[r * E_L + j] - s_g[r * E_L];
     }
   }
-  const int t = tile * kRouteTile + lane;
   if (t < T) {
-    for (int k = 0; k < K; ++k) {
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (k >= K) continue;
       const size_t q = (size_t)t * K + k;
-      const int e = ids[q];
       int drk = -1, drw = -1;
       uint8_t drop = 0;
-      if (e >= 0 && e < N) {
-        const int p = base[(size_t)e * ntiles + tile] + (int)rank_ws[q];
-        if (p < C) {
-          const int r = e / E_L;
+      if (p[k] >= 0) {
+        if (p[k] < C) {
+          const int r = e[k] / E_L;
           drk = r;
-          drw = s_g[e] - s_g[r * E_L] + p;
+          drw = s_g[e[k]] - s_g[r * E_L] + p[k];
           if (row_src != nullptr && r == ep_rank) row_src[drw] = (int32_t)q;
         } else {
           drop = 1;
@@ -238,15 +390,25 @@ __global__ __launch_bounds__(64) void k_assign(
 }
 
 template <int KM>
-void launch_tile(const moe_shape_t &s, const float *logits, const int32_t *ids_in,
-                 const moe_route_out_t &o, int32_t *hist, uint8_t *rank_ws, int ntiles,
-                 hipStream_t st) {
+int launch_route_km(const moe_shape_t &s, const float *logits, const int32_t *ids_in,
+                    const moe_route_out_t &o, int32_t *hist, uint8_t *rank_ws, int ntiles,
+                    hipStream_t st) {
   if (logits != nullptr)
-    hipLaunchKernelGGL((k_route_tile<KM, true>), dim3(ntiles), dim3(64), 0, st, logits,
-                       nullptr, o.topk_idx, o.topk_w, hist, rank_ws, s.T, s.N, s.K, ntiles);
+    hipLaunchKernelGGL((k_route_tile<KM, true>), dim3(ntiles), dim3(64 * kRouteWaves), 0, st,
+                       logits, nullptr, o.topk_idx, o.topk_w, hist, rank_ws, s.T, s.N, s.K,
+                       ntiles);
   else
-    hipLaunchKernelGGL((k_route_tile<KM, false>), dim3(ntiles), dim3(64), 0, st, nullptr,
-                       ids_in, nullptr, nullptr, hist, rank_ws, s.T, s.N, s.K, ntiles);
+    hipLaunchKernelGGL((k_route_tile<KM, false>), dim3(ntiles), dim3(64 * kRouteWaves), 0, st,
+                       nullptr, ids_in, nullptr, nullptr, hist, rank_ws, s.T, s.N, s.K, ntiles);
+  if (launch_status() != MOE_OK) return MOE_EHIP;
+  hipLaunchKernelGGL(k_tile_scan, dim3(s.N), dim3(256), 0, st, hist, o.counts, ntiles);
+  if (launch_status() != MOE_OK) return MOE_EHIP;
+  const int32_t *ids = logits != nullptr ? o.topk_idx : ids_in;
+  const int E_L = s.N / s.ep_size;
+  hipLaunchKernelGGL((k_assign<KM>), dim3(ntiles), dim3(64), 0, st, ids, hist, rank_ws, o.counts,
+                     o.dest_rank, o.dest_row, o.drop_mask, o.offsets, o.row_src, s.T, s.N,
+                     s.K, s.capacity, E_L, s.ep_size, s.ep_rank, ntiles);
+  return launch_status();
 }
 
 }  // namespace
@@ -256,19 +418,10 @@ int launch_route(const moe_shape_t &s, const float *logits, const int32_t *ids_i
   const int ntiles = route_tiles(s);
   int32_t *hist = static_cast<int32_t *>(ws);
   uint8_t *rank_ws = reinterpret_cast<uint8_t *>(hist + (size_t)s.N * ntiles);
-  if (s.K <= 2) launch_tile<2>(s, logits, ids_in, o, hist, rank_ws, ntiles, st);
-  else if (s.K <= 4) launch_tile<4>(s, logits, ids_in, o, hist, rank_ws, ntiles, st);
-  else if (s.K <= 8) launch_tile<8>(s, logits, ids_in, o, hist, rank_ws, ntiles, st);
-  else launch_tile<16>(s, logits, ids_in, o, hist, rank_ws, ntiles, st);
-  if (launch_status() != MOE_OK) return MOE_EHIP;
-  hipLaunchKernelGGL(k_tile_scan, dim3(s.N), dim3(256), 0, st, hist, o.counts, ntiles);
-  if (launch_status() != MOE_OK) return MOE_EHIP;
-  const int32_t *ids = logits != nullptr ? o.topk_idx : ids_in;
-  const int E_L = s.N / s.ep_size;
-  hipLaunchKernelGGL(k_assign, dim3(ntiles), dim3(64), 0, st, ids, hist, rank_ws, o.counts,
-                     o.dest_rank, o.dest_row, o.drop_mask, o.offsets, o.row_src, s.T, s.N,
-                     s.K, s.capacity, E_L, s.ep_size, s.ep_rank, ntiles);
-  return launch_status();
+  if (s.K <= 2) return launch_route_km<2>(s, logits, ids_in, o, hist, rank_ws, ntiles, st);
+  if (s.K <= 4) return launch_route_km<4>(s, logits, ids_in, o, hist, rank_ws, ntiles, st);
+  if (s.K <= 8) return launch_route_km<8>(s, logits, ids_in, o, hist, rank_ws, ntiles, st);
+  return launch_route_km<16>(s, logits, ids_in, o, hist, rank_ws, ntiles, st);
 }
 
 }  // namespace moe

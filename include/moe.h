@@ -24,7 +24,7 @@
  *   - Only host arguments are validated. Return value 0 = success, otherwise
  *     one of the negative MOE_E* codes below; nothing is enqueued on error.
  *   - Device-data preconditions that are NOT checked (checking would need a
- *     device-to-host read): logits are finite; moe_route_map ids lie in
+ *     device-to-host read): moe_route_map ids lie in
  *     [-1, N) and the valid ids of one token are distinct; buf, h, y and out
  *     do not alias each other or the inputs.
  *   - Expert placement is contiguous: rank r owns global experts
@@ -109,7 +109,9 @@ int moe_route_workspace_size(const moe_shape_t *shape, size_t *bytes);
 
 /* Top-K softmax gating and the route-map builder.
  * logits [T,N] fp32 (device). For each token: the K largest logits (ties ->
- * lower expert id, -0.0 == +0.0), their softmax weights (Olmo-core MoE report
+ * lower expert id, -0.0 == +0.0; -inf ranks below every number and NaN after
+ * every number, so any input selects K distinct experts; weights that meet
+ * inf - inf or NaN come out NaN), their softmax weights (Olmo-core MoE report
  * Sec. 05 Fig. 15: K ids and K weights per token, descending, summing to one),
  * then counts, capacity admission in token order, offsets and the route map
  * (Sec. 5.4, Fig. 16). All outputs except row_src are required; ws/ws_bytes

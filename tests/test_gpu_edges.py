@@ -11,7 +11,8 @@ import torch
 import combine_top_softmax_amd as moe
 from combine_top_softmax_amd.workloads import LayerConfig, make_inputs, random_ids
 from oracle import moe_oracle as orc
-from gpu_util import assert_rows_close, check_route, is_poison, poison_, to_np, tol_of
+from gpu_util import (assert_rows_close, check_route, is_poison, oracle_route, poison_,
+                      route_gpu, to_np, tol_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +74,35 @@ def test_maximum_expert_count_and_top_k():
     assert_rows_close(to_np(out), ref["out"], tol_of(cfg.dtype), "out")
 
 
+@pytest.mark.parametrize("N,K", [(24, 5), (22, 3), (64, 8), (200, 16)])
+def test_route_special_logits_match_oracle(N, K):
+    """Ties, signed zeros, -inf, +inf and NaN logits: the selection order of a
+    stable sort of -logit (NaN last), the oracle's softmax (NaN where it gives
+    NaN), and the route map that follows."""
+    T = 300
+    cfg = LayerConfig("special_logits", T=T, d=8, N=N, K=K, F=8, cf=Fraction(1), dtype="f32",
+                      ep_size=2, ep_rank=1, seed=50 + N)
+    rng = np.random.default_rng(cfg.seed)
+    L = rng.standard_normal((T, N)).astype(np.float32)
+    vals = np.array([np.nan, -np.inf, np.inf, -0.0, 0.0, 1.0, -1.0], dtype=np.float32)
+    mask = rng.random((T, N)) < 0.3
+    L[mask] = rng.choice(vals, size=int(mask.sum()))
+    L[0] = np.nan
+    L[1] = -np.inf
+    L[2] = 0.0
+    L[2, ::2] = -0.0
+    L[3] = -np.inf
+    L[3, :K - 1] = 1.5                     # fewer than K finite logits
+    L[4] = rng.choice(np.array([0.5, 0.25], dtype=np.float32), size=N)   # many ties
+    logits = torch.from_numpy(L)
+    print(f"[case] special logits N={N} K={K}", flush=True)
+    shape = moe.MoeShape.from_config(cfg)
+    out = route_gpu(shape, logits.cuda())
+    with np.errstate(invalid="ignore"):       # inf - inf in the weights of such rows
+        ref = oracle_route(cfg, logits)
+    check_route(out, ref, shape)
+
+
 def test_route_map_maximum_sizes_with_invalid():
     T, N, K, C, ep = 3000, 1024, 16, 60, 8
     ids = random_ids(T, N, K, seed=43, invalid_frac=0.05)
@@ -81,6 +111,22 @@ def test_route_map_maximum_sizes_with_invalid():
     ws = torch.empty(moe.moe_route_workspace_size(shape), dtype=torch.uint8, device="cuda")
     moe.moe_route_map(shape, ids.cuda(), out, ws)
     ref = orc.route_map(ids.numpy(), N, ep, C, 5)
+    torch.cuda.synchronize()
+    for k in ("counts", "offsets", "dest_rank", "dest_row", "drop_mask", "row_src"):
+        np.testing.assert_array_equal(to_np(getattr(out, k)), ref[k], err_msg=k)
+
+
+def test_route_map_long_batch_tile_scan_past_register_run():
+    """150000 tokens = 2344 route tiles: each tile-scan thread takes 10 tiles,
+    past the 8 it keeps in registers."""
+    T, N, K, C, ep = 150000, 8, 2, 20000, 2
+    ids = random_ids(T, N, K, seed=45, invalid_frac=0.05)
+    print(f"[case] route map T={T}", flush=True)
+    shape = moe.MoeShape(T=T, d=8, N=N, K=K, F=8, ep_size=ep, ep_rank=1, capacity=C, dtype="f32")
+    out = moe.RouteOut.empty(shape, "cuda")
+    ws = torch.empty(moe.moe_route_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    moe.moe_route_map(shape, ids.cuda(), out, ws)
+    ref = orc.route_map(ids.numpy(), N, ep, C, 1)
     torch.cuda.synchronize()
     for k in ("counts", "offsets", "dest_rank", "dest_row", "drop_mask", "row_src"):
         np.testing.assert_array_equal(to_np(getattr(out, k)), ref[k], err_msg=k)

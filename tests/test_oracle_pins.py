@@ -70,6 +70,35 @@ def test_topk_signed_zero_tie_falls_back_to_id():
     assert idx.tolist() == [[0, 1], [0, 1]]
 
 
+def _beats_nan_last(a, ia, b, ib):
+    """a (expert ia) ranks ahead of b (expert ib): numbers by value (IEEE
+    comparison, so -0.0 == +0.0 and -inf is the smallest), NaN after every
+    number, ties (NaN with NaN included) by the lower id."""
+    na, nb = math.isnan(a), math.isnan(b)
+    if na or nb:
+        return (nb and not na) or (na and nb and ia < ib)
+    return a > b or (a == b and ia < ib)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_topk_nonfinite_logits_rank_nan_last(seed):
+    rng = np.random.default_rng(100 + seed)
+    T, N = 60, 9
+    vals = np.array([np.nan, -np.inf, np.inf, -0.0, 0.0, -1.0, 1.0, 2.5], dtype=np.float32)
+    L = rng.choice(vals, size=(T, N)).astype(np.float32)
+    L[0] = np.nan
+    L[1] = -np.inf
+    for K in (1, 3, N):
+        with np.errstate(invalid="ignore"):   # inf - inf in the weights of such rows
+            idx, _ = orc.topk_softmax(L, K)
+        for t in range(T):
+            row = [float(v) for v in L[t]]
+            ranks = [sum(1 for e2 in range(N) if _beats_nan_last(row[e2], e2, row[e], e))
+                     for e in range(N)]
+            expect = sorted(range(N), key=lambda e: ranks[e])[:K]
+            assert list(idx[t]) == expect
+
+
 def test_topk_full_k_is_a_sorted_permutation():
     rng = np.random.default_rng(3)
     L = rng.standard_normal((30, 11)).astype(np.float32)
