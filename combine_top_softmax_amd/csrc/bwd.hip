@@ -198,7 +198,7 @@ __device__ __forceinline__ void store_elem(const GemmArgs &p, const Work &w, int
       g = gr[col];
       u = gr[p.F + col];
     }
-    const float s = 1.0f / (1.0f + __expf(-g));
+    const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
     const float dg = v * u * s * (1.0f + g * (1.0f - s));
     const float du = v * g * s;
     if constexpr (sizeof(T) == 2) {
@@ -693,7 +693,7 @@ __global__ __launch_bounds__(bt::NT, 1) void k_gemm_bwd_big(GemmArgs p) {
             const float dh = (e < 2) ? lo[2 * e + hh] : hi[2 * (e - 2) + hh];
             const float g = hh ? bf16_hi(gv[e]) : bf16_lo(gv[e]);
             const float u = hh ? bf16_hi(uv[e]) : bf16_lo(uv[e]);
-            const float s = 1.0f / (1.0f + __expf(-g));
+            const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
             o[0][hh] = dh * u * s * (1.0f + g * (1.0f - s));
             o[1][hh] = dh * g * s;
           }

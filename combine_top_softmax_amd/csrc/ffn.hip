@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(
       if (GATE_UP) {
         const int col = n0 + wn * 32 + fr;
         const float g = acc[ms][0][r], u = acc[ms][1][r];
-        const float hv = g / (1.0f + __expf(-g)) * u;
+        const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
         if (col < Nout) orow[col] = f2bf(hv);
       } else {
 #pragma unroll
