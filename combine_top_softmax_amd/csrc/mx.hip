@@ -55,37 +55,29 @@ __device__ __forceinline__ int mx_shared_exp(float amax) {
   return max(-127, min(127, e - 1 - 8));
 }
 
-// E4M3 code of v (v already divided by the block scale): nearest value, ties
-// to the even code, saturating at 448; the sign bit follows v's sign.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
-  const float a = fabsf(v);
-  uint32_t c;
-  if (a >= 448.f) {
-    c = 0x7E;
-  } else if (a < 0.015625f) {                 // below 2^-6: multiples of 2^-9
-    c = (uint32_t)rintf(a * 512.f);
-  } else {
-    int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;   // -6 .. 8 (a is normal)
-    const float m = __uint_as_float((__float_as_uint(a) & 0x007FFFFFu) | 0x3F800000u);
-    uint32_t mant = (uint32_t)rintf((m - 1.f) * 8.f);
-    if (mant == 8) {
-      mant = 0;
-      ++e;
-    }
-    c = ((uint32_t)(e + 7) << 3) | mant;
-  }
-  return c | sign;
+// E4M3 codes of v already divided by the block scale: nearest value, ties to
+// the even code, saturating at 448, the sign bit from v's sign. The hardware
+// fp32 -> fp8 conversion (OCP E4M3, round to nearest even) does the rounding
+// once v is clamped to [-448, 448] (med3 keeps -0.0); checked on the device
+// bit for bit against a direct encoding of that rule over every finite bf16
+// value and shared exponents -140 .. 147. Codes of (a, b) land in bytes
+// 2*HI and 2*HI + 1 of the result; the other bytes come from `old`.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b, uint32_t old) {
+  const float ca = __builtin_amdgcn_fmed3f(a, -448.f, 448.f);
+  const float cb = __builtin_amdgcn_fmed3f(b, -448.f, 448.f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, (int)old, HI);
 }
 
 // Codes of 8 bf16 values (two packed per dword) over the scale 2^se.
 __device__ __forceinline__ u32x2_t quant8(const u32x4_t v, int se) {
-  u32x2_t o = {0, 0};
+  u32x2_t o;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t lo = e4m3_code(ldexpf(bf16_lo(v[e]), -se));
-    const uint32_t hi = e4m3_code(ldexpf(bf16_hi(v[e]), -se));
-    o[e >> 1] |= (lo | (hi << 8)) << ((e & 1) * 16);
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t w =
+        e4m3_pair<false>(ldexpf(bf16_lo(v[2 * h]), -se), ldexpf(bf16_hi(v[2 * h]), -se), 0u);
+    o[h] = e4m3_pair<true>(ldexpf(bf16_lo(v[2 * h + 1]), -se), ldexpf(bf16_hi(v[2 * h + 1]), -se),
+                           w);
   }
   return o;
 }
@@ -213,19 +205,25 @@ __device__ __forceinline__ void mx_step(const MxCtx &c, int k0, int wv,
   // shifted by one byte in lanes 32-63: lane group g needs blocks g (first
   // K slice) and 2 + g (second), now bytes 0 and 2 for both groups, which the
   // MFMA selects with op_sel
+  // Read in the order of first use by the MFMA sequence (each fragment with
+  // its rows' scale dword: A0 B0 B1 A1 A2 A3), so that the first MFMAs of the
+  // step wait only for the oldest reads instead of for all of them.
   uint32_t sa[mxg::TM], sb[mxg::TN];
   const int gsh = 8 * g;
-#pragma unroll
-  for (int i = 0; i < mxg::TM; ++i)
-    sa[i] = *reinterpret_cast<const uint32_t *>(rd + c.sa_lds[i]) >> gsh;
-#pragma unroll
-  for (int j = 0; j < mxg::TN; ++j)
-    sb[j] = *reinterpret_cast<const uint32_t *>(rd + c.sb_lds[j]) >> gsh;
   i32x8_t fra[mxg::TM], frb[2][mxg::TN];
+  constexpr FragOrder<mxg::TM, mxg::TN> ord{};
 #pragma unroll
-  for (int i = 0; i < VT; ++i) fra[i] = frag(c.fa[i], 0);
-#pragma unroll
-  for (int j = 0; j < mxg::TN; ++j) frb[0][j] = frag(c.fb[j], 0);
+  for (int n = 0; n < mxg::TM + mxg::TN; ++n) {
+    const int f = ord.q[n];
+    if (f < mxg::TM) {
+      sa[f] = *reinterpret_cast<const uint32_t *>(rd + c.sa_lds[f]) >> gsh;
+      if (f < VT) fra[f] = frag(c.fa[f], 0);
+    } else {
+      const int j = f - mxg::TM;
+      sb[j] = *reinterpret_cast<const uint32_t *>(rd + c.sb_lds[j]) >> gsh;
+      frb[0][j] = frag(c.fb[j], 0);
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ks = 0; ks < mxg::KS; ++ks) {
