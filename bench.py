@@ -77,27 +77,32 @@ def cpu_baseline(cfg, target_s: float) -> dict:
     from combine_top_softmax_amd.workloads import make_inputs
     from oracle import moe_oracle as orc
 
-    def run(T_s):
+    def run(T_s, repeats=1):
         c = cfg.with_(T=T_s)
         inp = make_inputs(c, "cpu")
         args = (inp.logits.numpy(), inp.x.double().numpy(), inp.w_gu.double().numpy(),
                 inp.w_d.double().numpy(), c.K, c.capacity, c.ep_size, c.ep_rank, c.dtype)
-        t0 = time.perf_counter()
-        ref = orc.moe_layer(*args)
-        dt = time.perf_counter() - t0
-        return int(ref["offsets"][c.ep_rank, -1]), dt
+        times = []
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            ref = orc.moe_layer(*args)
+            times.append(time.perf_counter() - t0)
+        return int(ref["offsets"][c.ep_rank, -1]), sorted(times)[len(times) // 2], len(times)
 
     T_s = min(cfg.T, 256)
-    rows, dt = run(T_s)
+    rows, dt, n = run(T_s)
     if dt < target_s / 3 and T_s < cfg.T:
         T_s = min(cfg.T, max(T_s + 1, int(T_s * target_s / max(dt, 1e-3))))
-        rows, dt = run(T_s)
+        rows, dt, n = run(T_s)
+    if T_s == cfg.T and dt < target_s / 3:
+        # the whole workload is the sample: repeat it up to the time budget
+        rows, dt, n = run(T_s, repeats=max(1, min(5, int(target_s / max(dt, 1e-3)))))
     threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
     return {"value": rows / dt, "unit": "token-rows/s", "cores": int(threads), "kind": "oracle",
             "sample": f"whole layer (route, dispatch, FFN, combine) on a {T_s}-token layer of "
                       f"the {cfg.name} shape, same input recipe, capacity recomputed for {T_s} "
-                      f"tokens: {rows} routed rows in {dt:.2f} s; NumPy float64, "
-                      f"BLAS threads={threads}"}
+                      f"tokens: {rows} routed rows in {dt:.2f} s (median of {n} runs); "
+                      f"NumPy float64, BLAS threads={threads}"}
 
 
 MX_STAGES = ["route", "dispatch_mx", "up_mx", "down_mx", "combine"]
