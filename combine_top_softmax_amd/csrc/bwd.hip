@@ -12,8 +12,8 @@
 // Kernels:
 //   k_combine_bwd  wave per token: reads dOut[t] once per row segment, writes
 //                  w * dOut[t] to the dY row of each kept local route and the
-//                  dot <dOut[t], Y[row]> as that route's weight gradient (0 for
-//                  every other route).
+//                  dot <dOut[t], Y[row]> (a DPP wave sum) as that route's
+//                  weight gradient (0 for every other route).
 //   k_route_bwd    wave per token: logit gradient through the softmax over the
 //                  K selected logits, zero on the experts not selected.
 //   k_gemm_bwd     (bf16, MFMA) / k_gemm_bwd_f32 (fp32, SIMT): one grouped
@@ -45,14 +45,31 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsPerBlock = 4;   // 4 waves = 4 token rows per 256-thread block
 
+// v plus the DPP-moved value of v (lanes without a source add 0).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float add_dpp(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                 0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Sum of v over the 64 lanes, returned to every lane: the DPP inclusive scan
+// (shifts by 1, 2, 4, 8 inside each row of 16, then the row-15 and row-31
+// broadcasts) leaves the total in lane 63. All lanes must be active.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v = add_dpp<0x111, 0xf>(v);   // row_shr:1
+  v = add_dpp<0x112, 0xf>(v);   // row_shr:2
+  v = add_dpp<0x114, 0xf>(v);   // row_shr:4
+  v = add_dpp<0x118, 0xf>(v);   // row_shr:8
+  v = add_dpp<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v = add_dpp<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // ------------------------------------------------------------ combine backward
-template <bool BF16, int NV>
+// The token's route metadata is read once (lane k: route k) and a ballot marks
+// the kept local routes, taken two at a time in k order with both Y rows loaded
+// before either is used. FULL: the row is a whole number of segments.
+template <bool BF16, int NV, bool FULL>
 __global__ __launch_bounds__(256) void k_combine_bwd(
     const u32x4_t *__restrict__ dout, const u32x4_t *__restrict__ y,
     const int32_t *__restrict__ dest_rank, const int32_t *__restrict__ dest_row,
@@ -61,46 +78,77 @@ __global__ __launch_bounds__(256) void k_combine_bwd(
   const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6));
   if (t >= T) return;
+  const size_t q0 = (size_t)t * K;
+  int m_rank = -1, m_row = 0;
+  float m_w = 0.f;
+  if (lane < K) {
+    m_rank = dest_rank[q0 + lane];
+    m_row = dest_row[q0 + lane];
+    m_w = w[q0 + lane];
+  }
+  const uint64_t local = __ballot(m_rank == ep_rank);
   float dw_mine = 0.f;   // lane k < K accumulates route k's weight gradient
+  // dY row segment = w * dOut; returns this lane's part of <dOut, Y[row]>
+  auto route = [&](const u32x4_t (&g)[NV], const u32x4_t (&yv)[NV], size_t row, float wk,
+                   int seg) {
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = seg + i * 64 + lane;
+      if (!FULL && c >= nvec) continue;
+      u32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (BF16) {
+          const float g0 = bf16_lo(g[i][e]), g1 = bf16_hi(g[i][e]);
+          dot = fmaf(g0, bf16_lo(yv[i][e]), dot);
+          dot = fmaf(g1, bf16_hi(yv[i][e]), dot);
+          o[e] = pack_bf16x2(wk * g0, wk * g1);
+        } else {
+          const float g0 = __uint_as_float(g[i][e]);
+          dot = fmaf(g0, __uint_as_float(yv[i][e]), dot);
+          o[e] = __float_as_uint(wk * g0);
+        }
+      }
+      dy[row * nvec + c] = o;
+    }
+    return dot;
+  };
   for (int seg = 0; seg < nvec; seg += 64 * NV) {
     u32x4_t g[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c = seg + i * 64 + lane;
-      g[i] = (c < nvec) ? dout[(size_t)t * nvec + c] : u32x4_t{0, 0, 0, 0};
+      g[i] = (FULL || c < nvec) ? dout[(size_t)t * nvec + c] : u32x4_t{0, 0, 0, 0};
     }
-    for (int k = 0; k < K; ++k) {
-      const size_t q = (size_t)t * K + k;
-      if (dest_rank[q] != ep_rank) continue;
-      const size_t row = (size_t)dest_row[q];
-      const float wk = w[q];
-      float dot = 0.f;
+    for (uint64_t rest = local; rest != 0;) {
+      const int ka = __builtin_ctzll(rest);
+      rest &= rest - 1;
+      const bool hb = rest != 0;
+      const int kb = hb ? __builtin_ctzll(rest) : ka;
+      if (hb) rest &= rest - 1;
+      const size_t ra = (size_t)__builtin_amdgcn_readlane(m_row, ka);
+      const size_t rb = (size_t)__builtin_amdgcn_readlane(m_row, kb);
+      u32x4_t ya[NV], yb[NV];
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int c = seg + i * 64 + lane;
-        if (c >= nvec) continue;
-        const u32x4_t yv = y[row * nvec + c];
-        u32x4_t o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (BF16) {
-            const float g0 = bf16_lo(g[i][e]), g1 = bf16_hi(g[i][e]);
-            dot = fmaf(g0, bf16_lo(yv[e]), dot);
-            dot = fmaf(g1, bf16_hi(yv[e]), dot);
-            o[e] = pack_bf16x2(wk * g0, wk * g1);
-          } else {
-            const float g0 = __uint_as_float(g[i][e]);
-            dot = fmaf(g0, __uint_as_float(yv[e]), dot);
-            o[e] = __float_as_uint(wk * g0);
-          }
+        if (FULL || c < nvec) {
+          ya[i] = y[ra * nvec + c];
+          if (hb) yb[i] = y[rb * nvec + c];
         }
-        dy[row * nvec + c] = o;
       }
-      dot = wave_sum(dot);
-      if (lane == k) dw_mine += dot;
+      const float da = wave_sum(route(g, ya, ra, __builtin_bit_cast(float,
+                                __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_w), ka)), seg));
+      if (lane == ka) dw_mine += da;
+      if (hb) {
+        const float db = wave_sum(route(g, yb, rb, __builtin_bit_cast(float,
+                                  __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_w), kb)), seg));
+        if (lane == kb) dw_mine += db;
+      }
     }
   }
-  if (lane < K) dw[(size_t)t * K + lane] = dw_mine;
+  if (lane < K) dw[q0 + lane] = dw_mine;
 }
 
 // ------------------------------------------------------------ router backward
@@ -801,15 +849,15 @@ void launch_mode(const moe_shape_t &s, GemmArgs p, hipStream_t st) {
   else hipLaunchKernelGGL(k_gemm_bwd_f32<MODE>, grid, dim3(256), 0, st, p);
 }
 
-template <bool BF16>
+template <bool BF16, bool FULL>
 void combine_bwd_nv(int nv, dim3 grid, hipStream_t st, const u32x4_t *g, const u32x4_t *y,
                     const int32_t *dr, const int32_t *drow, const float *w, u32x4_t *o,
                     float *dw, const moe_shape_t &s, int nvec) {
   switch (nv) {
-    case 1: hipLaunchKernelGGL((k_combine_bwd<BF16, 1>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
-    case 2: hipLaunchKernelGGL((k_combine_bwd<BF16, 2>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
-    case 4: hipLaunchKernelGGL((k_combine_bwd<BF16, 4>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
-    default: hipLaunchKernelGGL((k_combine_bwd<BF16, 8>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
+    case 1: hipLaunchKernelGGL((k_combine_bwd<BF16, 1, FULL>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
+    case 2: hipLaunchKernelGGL((k_combine_bwd<BF16, 2, FULL>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
+    case 4: hipLaunchKernelGGL((k_combine_bwd<BF16, 4, FULL>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
+    default: hipLaunchKernelGGL((k_combine_bwd<BF16, 8, FULL>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
   }
 }
 
@@ -825,10 +873,14 @@ int launch_combine_bwd(const moe_shape_t &s, const void *dout, const void *y,
   const u32x4_t *g = static_cast<const u32x4_t *>(dout);
   const u32x4_t *yv = static_cast<const u32x4_t *>(y);
   u32x4_t *o = static_cast<u32x4_t *>(dy);
-  if (s.dtype == MOE_BF16)
-    combine_bwd_nv<true>(nv, grid, st, g, yv, dest_rank, dest_row, w, o, dw, s, nvec);
-  else
-    combine_bwd_nv<false>(nv, grid, st, g, yv, dest_rank, dest_row, w, o, dw, s, nvec);
+  const bool full = nvec % (64 * nv) == 0;
+  if (s.dtype == MOE_BF16) {
+    if (full) combine_bwd_nv<true, true>(nv, grid, st, g, yv, dest_rank, dest_row, w, o, dw, s, nvec);
+    else combine_bwd_nv<true, false>(nv, grid, st, g, yv, dest_rank, dest_row, w, o, dw, s, nvec);
+  } else {
+    if (full) combine_bwd_nv<false, true>(nv, grid, st, g, yv, dest_rank, dest_row, w, o, dw, s, nvec);
+    else combine_bwd_nv<false, false>(nv, grid, st, g, yv, dest_rank, dest_row, w, o, dw, s, nvec);
+  }
   return launch_status();
 }
 
