@@ -221,7 +221,7 @@ def time_backward(args, layer, inp, stream, torch) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the expert-parallel exchange across GPUs is not part of it)", file=sys.stderr)
         sys.exit(2)
 
