@@ -131,10 +131,18 @@ __global__ __launch_bounds__(256) void k_quant_rows(
 }
 
 // ------------------------------------------------------------ MX grouped GEMM
+// Waves per MX block: 8 (two per SIMD, 128 x 64 wave tiles) or 4 (one per
+// SIMD, 128 x 128 wave tiles, a third fewer LDS fragment bytes per flop). 8
+// measured 1-5% faster than 4 on the named workloads: with two LDS stages
+// and a full wait per step, a second wave per SIMD covers more of the stalls.
+#ifndef MOE_MX_WAVES
+#define MOE_MX_WAVES 8
+#endif
 namespace mxg {
-constexpr int BM = 256, BW = 256, BK = 128, NW = 8, NT = 64 * NW;
-constexpr int WAVES_N = 4, WTN = BW / WAVES_N;   // 64 weight rows per wave
-constexpr int TM = 4, TN = WTN / 32;             // 4 x 2 MFMA tiles per wave
+constexpr int BM = 256, BW = 256, BK = 128, NW = MOE_MX_WAVES, NT = 64 * NW;
+constexpr int WAVES_N = NW / 2, WTN = BW / WAVES_N;   // weight rows per wave
+constexpr int TM = 4, TN = WTN / 32;             // 4 x TN MFMA tiles per wave
+constexpr int SPW = 8 / NW;                      // scale-dword loads per wave and step
 constexpr int ROW_B = BK;                        // bytes per LDS row
 constexpr int RPI = 8;                           // rows per direct-load instruction
 constexpr int NA = BM / RPI / NW, NB = BW / RPI / NW, L = NA + NB;
@@ -145,10 +153,11 @@ constexpr int STAGE = SC_OFF + (BM + BW) * 4;
 }  // namespace mxg
 
 struct MxCtx {
-  const uint8_t *A, *W, *S;   // S: this wave's scale source (A's or the expert's W scales)
+  const uint8_t *A, *W;
+  const uint8_t *S[mxg::SPW];   // this wave's scale sources (A's or the expert's W scales)
   uint32_t a_off[mxg::NA], b_off[mxg::NB];
-  uint32_t s_off;             // byte offset of this lane's scale row (step 0)
-  int s_dst;                  // LDS byte offset of this wave's scale dwords
+  uint32_t s_off[mxg::SPW];     // byte offset of this lane's scale row (step 0)
+  int s_dst[mxg::SPW];          // LDS byte offset of this wave's scale dwords
   int fa[mxg::TM], fb[mxg::TN];
   int sa_lds[mxg::TM], sb_lds[mxg::TN];
   int sw;
@@ -156,7 +165,9 @@ struct MxCtx {
 };
 
 __device__ __forceinline__ void mx_issue(const MxCtx &c, int k0, int wv, uint32_t stage) {
-  dma4(c.S + (uint32_t)(c.s_off + (k0 >> 5)), stage + c.s_dst);
+#pragma unroll
+  for (int j = 0; j < mxg::SPW; ++j)
+    dma4(c.S[j] + (uint32_t)(c.s_off[j] + (k0 >> 5)), stage + c.s_dst[j]);
 #pragma unroll
   for (int i = 0; i < mxg::NA; ++i)
     if (!((c.a_skip >> i) & 1))
@@ -180,7 +191,7 @@ __device__ __forceinline__ void mx_step(const MxCtx &c, int k0, int wv,
                                         uint32_t ld, const uint8_t *__restrict__ rd,
                                         int g, f32x16_t (&acc)[mxg::TM][mxg::TN]) {
   constexpr int MF = mxg::KS * mxg::TM * mxg::TN;   // 16
-  constexpr int L = mxg::L + 1;                     // + the scale load
+  constexpr int L = mxg::L + mxg::SPW;              // + the scale loads
   constexpr int GAP = MF / (2 * L) > 0 ? MF / (2 * L) : 1;
   // k0: the K offset (bytes) of the step loaded into `ld` (the caller repeats
   // the last step on the last iteration: no branch inside the step)
@@ -191,8 +202,10 @@ __device__ __forceinline__ void mx_step(const MxCtx &c, int k0, int wv,
     } else if (d < mxg::L)
       dma16(c.W + (uint32_t)(c.b_off[d - mxg::NA] + k0),
             ld + mxg::A_BYTES + (wv * mxg::NB + (d - mxg::NA)) * 1024);
-    else
-      dma4(c.S + (uint32_t)(c.s_off + (k0 >> 5)), ld + c.s_dst);
+    else {
+      const int j = d - mxg::L;
+      dma4(c.S[j] + (uint32_t)(c.s_off[j] + (k0 >> 5)), ld + c.s_dst[j]);
+    }
   };
   // chunks g and 2 + g of the 64-byte K slice ks of LDS row `off`
   auto frag = [&](int off, int ks) {
@@ -301,18 +314,21 @@ __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
     }
   }
   c.sw = chunk_swz<8>(fr);
-  // scale dwords of one step (4 blocks per row) through LDS: waves 0-3 load
-  // A's 256 rows, waves 4-7 the block's 256 weight rows, one dword per lane
-  {
-    const int r = (wv & 3) * 64 + lane;
-    if (wv < 4) {
-      c.S = As;
-      c.s_off = (uint32_t)min(tl.row0 + r, tl.row_end - 1) * (uint32_t)kb32;
-      c.s_dst = mxg::SC_OFF + (wv & 3) * 256;
+  // scale dwords of one step (4 blocks per row) through LDS, one dword per
+  // lane: scale load u = wv * SPW + j takes A's rows 64u .. 64u+63 for u < 4,
+  // else the block's weight rows 64(u-4) .. 64(u-4)+63
+#pragma unroll
+  for (int j = 0; j < mxg::SPW; ++j) {
+    const int u = wv * mxg::SPW + j;
+    const int r = (u & 3) * 64 + lane;
+    if (u < 4) {
+      c.S[j] = As;
+      c.s_off[j] = (uint32_t)min(tl.row0 + r, tl.row_end - 1) * (uint32_t)kb32;
+      c.s_dst[j] = mxg::SC_OFF + (u & 3) * 256;
     } else {
-      c.S = Ws + (size_t)tl.expert * Nw * kb32;
-      c.s_off = (uint32_t)wrow_of(r) * (uint32_t)kb32;
-      c.s_dst = mxg::SC_OFF + mxg::BM * 4 + (wv & 3) * 256;
+      c.S[j] = Ws + (size_t)tl.expert * Nw * kb32;
+      c.s_off[j] = (uint32_t)wrow_of(r) * (uint32_t)kb32;
+      c.s_dst[j] = mxg::SC_OFF + mxg::BM * 4 + (u & 3) * 256;
     }
   }
   // fragment rows and the LDS scale dwords that go with them
