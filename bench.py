@@ -41,7 +41,8 @@ def parse():
     p.add_argument("--no-mx", action="store_true",
                    help="skip the timing of the MXFP8 forward (reported beside the BF16 one)")
     p.add_argument("--traffic-probe", action="store_true",
-                   help="run 3 layer forwards, then 3 plain 512 MiB device copies (the "
+                   help="run 3 layer forwards, 3 up GEMMs that keep [G U], then 3 plain "
+                        "512 MiB device copies (the "
                         "calibration kernel for rocprofv3 FETCH_SIZE / WRITE_SIZE), and exit")
     return p.parse_args()
 
@@ -167,8 +168,9 @@ BWD_STAGES = ["combine_bwd", "expert_ffn_bwd_data", "dispatch_bwd", "route_bwd",
 
 def time_backward(args, layer, inp, stream, torch) -> dict:
     """Layer backward after the forward's buffers (same route map), in the
-    order MoELayer.backward issues it, timed with events between the calls.
-    Not part of ``value``."""
+    order MoELayer.backward issues it, timed with events between the calls;
+    then the same with [G U] kept by the forward's up GEMM (no recompute),
+    with that up GEMM timed beside the plain one. Not part of ``value``."""
     from combine_top_softmax_amd.workloads import random_rows
     import combine_top_softmax_amd as moe
     cfg = layer.shape
@@ -177,34 +179,64 @@ def time_backward(args, layer, inp, stream, torch) -> dict:
     layer.alloc_backward("cuda")
     s, r = layer.shape, layer.route
 
-    def bstep(ev=None):
+    dgu_sep = torch.empty_like(layer.gu)   # keeps the saved [G U] intact across steps
+
+    def bstep(ev=None, saved=False):
+        dgu = dgu_sep if saved else layer.gu
         if ev: ev[0].record(stream)
         moe.moe_combine_bwd(s, dout, layer.y, r.dest_rank, r.dest_row, r.topk_w, layer.dy,
                             layer.dw)
         if ev: ev[1].record(stream)
-        moe.moe_expert_ffn_bwd_data(s, layer.buf, r.offsets, inp.w_gu, inp.w_d, layer.dy,
-                                    layer.gu, layer.gu, layer.dx_rows)
+        if saved:
+            moe.moe_expert_ffn_bwd_data_saved_gu(s, r.offsets, inp.w_gu, inp.w_d, layer.dy,
+                                                 layer.gu, dgu, layer.dx_rows)
+        else:
+            moe.moe_expert_ffn_bwd_data(s, layer.buf, r.offsets, inp.w_gu, inp.w_d, layer.dy,
+                                        layer.gu, dgu, layer.dx_rows)
         if ev: ev[2].record(stream)
         moe.moe_dispatch_bwd(s, layer.dx_rows, r.dest_rank, r.dest_row, layer.dx)
         if ev: ev[3].record(stream)
         moe.moe_route_bwd(s, r.topk_idx, r.topk_w, layer.dw, layer.dlogits)
         if ev: ev[4].record(stream)
-        moe.moe_expert_ffn_bwd_weight(s, layer.buf, r.offsets, layer.h, layer.dy, layer.gu,
+        moe.moe_expert_ffn_bwd_weight(s, layer.buf, r.offsets, layer.h, layer.dy, dgu,
                                       layer.dw_gu, layer.dw_down)
         if ev: ev[5].record(stream)
 
-    for _ in range(args.warmup):
-        bstep()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.set_sync_debug_mode("error")
-    for i in range(args.steps):
-        bstep(evs[i])
-    torch.cuda.set_sync_debug_mode(0)
-    torch.cuda.synchronize()
-    ms = evs[0][0].elapsed_time(evs[-1][5]) / args.steps
-    st = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
-          for i, n in enumerate(BWD_STAGES)}
+    def run(saved):
+        for _ in range(args.warmup):
+            bstep(saved=saved)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
+               for _ in range(args.steps)]
+        torch.cuda.set_sync_debug_mode("error")
+        for i in range(args.steps):
+            bstep(evs[i], saved)
+        torch.cuda.set_sync_debug_mode(0)
+        torch.cuda.synchronize()
+        ms = evs[0][0].elapsed_time(evs[-1][5]) / args.steps
+        st = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+              for i, n in enumerate(BWD_STAGES)}
+        return ms, st
+
+    def time_up(save):
+        fn = (lambda: moe.moe_expert_up_save_gu(s, layer.buf, r.offsets, inp.w_gu, layer.h,
+                                                layer.gu)) if save else \
+             (lambda: moe.moe_expert_up(s, layer.buf, r.offsets, inp.w_gu, layer.h))
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms, st = run(saved=False)
+    # training pair with the forward keeping [G U]: the up GEMM's extra cost
+    # and the backward without the recompute
+    up_ms, up_save_ms = time_up(False), time_up(True)
+    ms_saved, st_saved = run(saved=True)
     R = int(r.offsets[s.ep_rank, -1].item())
     # data half: recomputed [G U] 4 R d F, dH 2 R d F, dX 4 R d F;
     # weight half: dW_d 2 R d F, dW_gu 4 R d F
@@ -215,7 +247,12 @@ def time_backward(args, layer, inp, stream, torch) -> dict:
             "expert_ffn_bwd_TFLOPs": round(12 * rdf / (t_data + t_wt) / 1e12, 1),
             "expert_ffn_bwd_TFLOPs_incl_recompute": round(16 * rdf / (t_data + t_wt) / 1e12, 1),
             "expert_ffn_bwd_data_TFLOPs": round(10 * rdf / t_data / 1e12, 1),
-            "expert_ffn_bwd_weight_TFLOPs": round(6 * rdf / t_wt / 1e12, 1)}
+            "expert_ffn_bwd_weight_TFLOPs": round(6 * rdf / t_wt / 1e12, 1),
+            "saved_gu": {"ms_per_step": round(ms_saved, 5),
+                         "stages_ms": {n: round(v, 5) for n, v in st_saved.items()},
+                         "expert_up_ms": round(up_ms, 5),
+                         "expert_up_save_gu_ms": round(up_save_ms, 5),
+                         "train_step_saving_ms": round(ms - ms_saved - (up_save_ms - up_ms), 5)}}
 
 
 def main():
@@ -239,6 +276,8 @@ def main():
     if args.traffic_probe:
         for _ in range(3):
             layer.forward(inp.logits, inp.x, inp.w_gu, inp.w_d)
+        for _ in range(3):   # the training up GEMM that also keeps [G U]
+            layer.up_step(inp.w_gu, save_gu=True)
         src = torch.empty(256 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):

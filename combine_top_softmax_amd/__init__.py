@@ -23,7 +23,8 @@ __all__ = [
     "MoeShape", "RouteOut", "MoELayer", "MoeError", "moe_route_workspace_size", "moe_route",
     "moe_route_map", "moe_dispatch_rows", "moe_expert_ffn", "moe_expert_up",
     "moe_expert_down", "moe_combine", "moe_combine_bwd", "moe_expert_ffn_bwd",
-    "moe_expert_ffn_bwd_data", "moe_expert_ffn_bwd_weight",
+    "moe_expert_ffn_bwd_data", "moe_expert_ffn_bwd_weight", "moe_expert_up_save_gu",
+    "moe_expert_ffn_bwd_data_saved_gu",
     "moe_dispatch_bwd", "moe_route_bwd", "moe_mx_quantize_rows", "moe_dispatch_rows_mx",
     "moe_expert_up_mx", "moe_expert_down_mx", "MxWeights", "moe_strerror", "moe_validate_shape",
 ]
@@ -200,6 +201,18 @@ def moe_expert_up(shape: MoeShape, buf, offsets, w_gu, h, stream=None) -> None:
     _abi.check("moe_expert_up", rc)
 
 
+def moe_expert_up_save_gu(shape: MoeShape, buf, offsets, w_gu, h, gu, stream=None) -> None:
+    dt = shape.torch_dtype
+    _need(buf, "buf", (shape.rows, shape.d), dt)
+    _ffn_checks(shape, offsets)
+    _need(w_gu, "w_gu", (shape.E_L, 2 * shape.F, shape.d), dt)
+    _need(h, "h", (shape.rows, shape.F), dt)
+    _need(gu, "gu", (shape.rows, 2 * shape.F), dt)
+    rc = _abi.load().moe_expert_up_save_gu(ctypes.byref(shape.c()), _ptr(buf), _ptr(offsets),
+                                           _ptr(w_gu), _ptr(h), _ptr(gu), _stream(stream))
+    _abi.check("moe_expert_up_save_gu", rc)
+
+
 def moe_expert_down(shape: MoeShape, h, offsets, w_down, y, stream=None) -> None:
     dt = shape.torch_dtype
     _need(h, "h", (shape.rows, shape.F), dt)
@@ -289,6 +302,22 @@ def moe_expert_ffn_bwd_data(shape: MoeShape, buf, offsets, w_gu, w_down, dy, gu,
         ctypes.byref(shape.c()), _ptr(buf), _ptr(offsets), _ptr(w_gu), _ptr(w_down), _ptr(dy),
         _ptr(gu), _ptr(dgu), _ptr(dx_rows), _stream(stream))
     _abi.check("moe_expert_ffn_bwd_data", rc)
+
+
+def moe_expert_ffn_bwd_data_saved_gu(shape: MoeShape, offsets, w_gu, w_down, dy, gu, dgu,
+                                     dx_rows, stream=None) -> None:
+    dt = shape.torch_dtype
+    _ffn_checks(shape, offsets)
+    _need(w_gu, "w_gu", (shape.E_L, 2 * shape.F, shape.d), dt)
+    _need(w_down, "w_down", (shape.E_L, shape.d, shape.F), dt)
+    _need(dy, "dy", (shape.rows, shape.d), dt)
+    _need(gu, "gu", (shape.rows, 2 * shape.F), dt)
+    _need(dgu, "dgu", (shape.rows, 2 * shape.F), dt)
+    _need(dx_rows, "dx_rows", (shape.rows, shape.d), dt)
+    rc = _abi.load().moe_expert_ffn_bwd_data_saved_gu(
+        ctypes.byref(shape.c()), _ptr(offsets), _ptr(w_gu), _ptr(w_down), _ptr(dy), _ptr(gu),
+        _ptr(dgu), _ptr(dx_rows), _stream(stream))
+    _abi.check("moe_expert_ffn_bwd_data_saved_gu", rc)
 
 
 def moe_expert_ffn_bwd_weight(shape: MoeShape, buf, offsets, h, dy, dgu, dw_gu, dw_down,
@@ -431,8 +460,15 @@ class MoELayer:
         r = self.route
         moe_dispatch_rows(self.shape, x, r.dest_rank, r.dest_row, self.buf, stream)
 
-    def up_step(self, w_gu, stream=None):
-        moe_expert_up(self.shape, self.buf, self.route.offsets, w_gu, self.h, stream)
+    def up_step(self, w_gu, stream=None, save_gu: bool = False):
+        if save_gu:
+            if not hasattr(self, "gu"):
+                self.alloc_backward(self.out.device)
+            moe_expert_up_save_gu(self.shape, self.buf, self.route.offsets, w_gu, self.h,
+                                  self.gu, stream)
+        else:
+            moe_expert_up(self.shape, self.buf, self.route.offsets, w_gu, self.h, stream)
+        self.gu_saved = save_gu
 
     def down_step(self, w_d, stream=None):
         moe_expert_down(self.shape, self.h, self.route.offsets, w_d, self.y, stream)
@@ -441,11 +477,14 @@ class MoELayer:
         r = self.route
         moe_combine(self.shape, self.y, r.dest_rank, r.dest_row, r.topk_w, self.out, stream)
 
-    def forward(self, logits, x, w_gu, w_d, stream=None) -> torch.Tensor:
+    def forward(self, logits, x, w_gu, w_d, stream=None, save_gu: bool = False) -> torch.Tensor:
+        """Route, dispatch, expert FFN, combine. ``save_gu`` (training): the up
+        GEMM also keeps the pre-activation [G U] rows, so that ``backward``
+        reads them instead of recomputing them."""
         self.route_step(logits, stream)
         self.dispatch_step(x, stream)
-        moe_expert_ffn(self.shape, self.buf, self.route.offsets, w_gu, w_d, self.h, self.y,
-                       stream)
+        self.up_step(w_gu, stream, save_gu)
+        self.down_step(w_d, stream)
         self.combine_step(stream)
         return self.out
 
@@ -476,6 +515,7 @@ class MoELayer:
         GEMMs on the quantized weights, BF16 combine."""
         if not hasattr(self, "qbuf"):
             self.alloc_mx(self.out.device)
+        self.gu_saved = False
         self.route_step(logits, stream)
         self.dispatch_mx_step(x, stream)
         self.up_mx_step(mxw, stream)
@@ -506,9 +546,16 @@ class MoELayer:
         s, r = self.shape, self.route
         moe_combine_bwd(s, dout, self.y, r.dest_rank, r.dest_row, r.topk_w, self.dy, self.dw,
                         stream)
-        # row gradients first, so dispatch backward reads dX rows while cached
-        moe_expert_ffn_bwd_data(s, self.buf, r.offsets, w_gu, w_d, self.dy, self.gu, self.gu,
-                                self.dx_rows, stream)
+        # row gradients first, so dispatch backward reads dX rows while cached;
+        # [G U] from the forward when it kept them, else recomputed (dgu
+        # overwrites gu in place either way)
+        if getattr(self, "gu_saved", False):
+            moe_expert_ffn_bwd_data_saved_gu(s, r.offsets, w_gu, w_d, self.dy, self.gu, self.gu,
+                                             self.dx_rows, stream)
+            self.gu_saved = False
+        else:
+            moe_expert_ffn_bwd_data(s, self.buf, r.offsets, w_gu, w_d, self.dy, self.gu,
+                                    self.gu, self.dx_rows, stream)
         moe_dispatch_bwd(s, self.dx_rows, r.dest_rank, r.dest_row, self.dx, stream)
         moe_route_bwd(s, r.topk_idx, r.topk_w, self.dw, self.dlogits, stream)
         moe_expert_ffn_bwd_weight(s, self.buf, r.offsets, self.h, self.dy, self.gu, self.dw_gu,

@@ -42,11 +42,13 @@ SIGNATURES = {
     "moe_dispatch_rows": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_expert_ffn": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_up": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
+    "moe_expert_up_save_gu": (ctypes.c_int, [_SHAPE] + [_P] * 6),
     "moe_expert_down": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_combine": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P]),
     "moe_combine_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_bwd": (ctypes.c_int, [_SHAPE] + [_P] * 12),
     "moe_expert_ffn_bwd_data": (ctypes.c_int, [_SHAPE] + [_P] * 9),
+    "moe_expert_ffn_bwd_data_saved_gu": (ctypes.c_int, [_SHAPE] + [_P] * 8),
     "moe_expert_ffn_bwd_weight": (ctypes.c_int, [_SHAPE] + [_P] * 8),
     "moe_dispatch_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_route_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),

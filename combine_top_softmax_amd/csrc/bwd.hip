@@ -19,7 +19,7 @@
 //   k_gemm_bwd     (bf16, MFMA) / k_gemm_bwd_f32 (fp32, SIMT): one grouped
 //                  GEMM for the four products of the expert backward:
 //                    DH: dH = dY W_d per expert over its rows, fused with the
-//                        SwiGLU backward on the recomputed G, U -> [dG dU]
+//                        SwiGLU backward on G, U -> [dG dU]
 //                    DX: dX = [dG dU] W_gu per expert over its rows
 //                    WG: dW = P^T Q per expert, contracted over the expert's
 //                        rows (dW_d = dY^T H, dW_gu = [dG dU]^T X), fp32 out;
@@ -28,7 +28,8 @@
 //                  weight-gradient left operand is M-contiguous; the bf16
 //                  kernel transposes those tiles while writing them to LDS, so
 //                  every MFMA operand is read K-contiguous.
-// G, U are recomputed by the forward NT GEMM (no activation, 2F columns);
+// G, U are recomputed by the forward NT GEMM (no activation, 2F columns), or
+// taken from the rows the up GEMM kept during the forward;
 // dispatch backward is the forward combine kernel with unit weights.
 #include <type_traits>
 
@@ -192,7 +193,7 @@ struct GemmArgs {
   int64_t b_expert_stride;
   const int32_t *off;
   int E_L, M, N, Kdim;
-  const void *gu;   // DH: recomputed [G U] rows, [rows, 2F]
+  const void *gu;   // DH: pre-activation [G U] rows (recomputed or saved), [rows, 2F]
   int F;
   void *Out;
   int ldo;
@@ -931,11 +932,20 @@ int launch_expert_ffn_bwd_data(const moe_shape_t &s, const void *buf, const int3
                                const void *w_gu, const void *w_down, const void *dy, void *gu,
                                void *dgu, void *dx_rows, hipStream_t st) {
   const int E_L = s.N / s.ep_size;
-  const int d = s.d, F = s.F;
   const int32_t *off = offsets + (size_t)s.ep_rank * (E_L + 1);
   // 1. [G U] = X W_gu^T over the prefix rows (forward NT GEMM, no activation)
-  int rc = launch_gemm_nt(s, buf, w_gu, off, gu, d, 2 * F, st);
+  const int rc = launch_gemm_nt(s, buf, w_gu, off, gu, s.d, 2 * s.F, st);
   if (rc != MOE_OK) return rc;
+  return launch_expert_ffn_bwd_data_gu(s, offsets, w_gu, w_down, dy, gu, dgu, dx_rows, st);
+}
+
+int launch_expert_ffn_bwd_data_gu(const moe_shape_t &s, const int32_t *offsets, const void *w_gu,
+                                  const void *w_down, const void *dy, const void *gu, void *dgu,
+                                  void *dx_rows, hipStream_t st) {
+  const int E_L = s.N / s.ep_size;
+  const int d = s.d, F = s.F;
+  const int32_t *off = offsets + (size_t)s.ep_rank * (E_L + 1);
+  int rc;
   GemmArgs p{};
   p.off = off;
   p.E_L = E_L;

@@ -98,6 +98,12 @@ constexpr int kBW = 128;        // weight rows per block tile
 constexpr int kBK = 64;         // K per main-loop step
 constexpr int kLds = kBK + 8;   // padded LDS row (elements)
 
+// silu(g) * u of the fused up epilogue (the same expression wherever H is
+// formed from the accumulators, so H does not depend on the epilogue variant).
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 template <bool GATE_UP>
 __global__ __launch_bounds__(256, 2) void k_gemm_bf16(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(
       if (GATE_UP) {
         const int col = n0 + wn * 32 + fr;
         const float g = acc[ms][0][r], u = acc[ms][1][r];
-        const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+        const float hv = swiglu(g, u);
         if (col < Nout) orow[col] = f2bf(hv);
       } else {
 #pragma unroll
@@ -352,12 +358,13 @@ __device__ __forceinline__ void big_step(
 
 // Epilogue of the big-tile kernels (every wave past its last MFMA, every
 // direct load drained, the stages free).
-template <bool GATE_UP, int BM, int NW>
+template <bool GATE_UP, bool SAVE, int BM, int NW>
 __device__ __forceinline__ void big_epilogue(
     const f32x16_t (&acc)[BigTile<BM, 64, 2, NW>::TM][BigTile<BM, 64, 2, NW>::TN],
-    uint8_t *__restrict__ smem, const Tile &tl, uint16_t *__restrict__ Out, int Nout, int n0,
-    int wm, int wn) {
+    uint8_t *__restrict__ smem, const Tile &tl, uint16_t *__restrict__ Out,
+    uint16_t *__restrict__ GU, int Nout, int n0, int wm, int wn) {
   using P = BigTile<BM, 64, 2, NW>;
+  static_assert(!SAVE || GATE_UP, "only the gate/up product has a [G U] tile to keep");
   // Epilogue, staged through LDS so that global stores are whole 16-byte
   // vectors along output rows. The MFMAs take the weight fragment as their
   // first operand, so each 32x32 accumulator tile holds the transposed tile:
@@ -378,6 +385,85 @@ __device__ __forceinline__ void big_epilogue(
   auto stage_off = [](int row, int chunk) {   // byte offset of 16-byte chunk `chunk` of `row`
     return row * ROWB + ((chunk ^ (row & (CPR - 1))) << 4);
   };
+  if constexpr (SAVE) {
+    // H and the pre-activation G, U of the same columns (G from weight rows
+    // 0..BW/2-1 of the block, U from BW/2..BW-1), all rounded from the same
+    // accumulators, in two passes over half the rows (the wave's 32-row
+    // tiles 2p and 2p+1), so that every accumulator is read once: a pass
+    // stages [G U] rows (BW columns) and H rows (OUTC columns) of BM/2 block
+    // rows in the swizzled layout, then copies them out with 16-byte stores
+    // to GU[row, n0 + c] (gate half), GU[row, Nout + n0 + c] (up half) and
+    // Out[row, n0 + c].
+    constexpr int GROWB = P::BW * 2;
+    constexpr int GCPR = GROWB / 16;
+    constexpr int SR = BM / 2;                     // block rows staged per pass
+    constexpr int H_BASE = SR * GROWB;
+    static_assert(H_BASE + SR * ROWB <= 2 * P::A_BYTES + 2 * P::B_BYTES, "pass fits the stages");
+    auto gstage_off = [](int row, int chunk) {
+      return row * GROWB + ((chunk ^ (row & (GCPR - 1))) << 4);
+    };
+    const int nrows = min(BM, tl.row_end - tl.row0);
+    const int ncols = min(OUTC, Nout - n0);
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int tm = 2 * pass + t;
+        const int srow = wm * 64 + t * 32 + fr;    // staged row
+#pragma unroll
+        for (int tn = 0; tn < P::TN / 2; ++tn) {
+          const int col0 = wn * (P::WTN / 2) + tn * 32;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float gv[4], uv[4], hv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              gv[e] = acc[tm][tn][4 * g + e];
+              uv[e] = acc[tm][tn + P::TN / 2][4 * g + e];
+              hv[e] = swiglu(gv[e], uv[e]);
+            }
+            const int cb = (col0 + 8 * g + 4 * khalf) * 2;
+            uint2 w;
+            w.x = pack2_bf16(gv[0], gv[1]);
+            w.y = pack2_bf16(gv[2], gv[3]);
+            *reinterpret_cast<uint2 *>(smem + gstage_off(srow, cb >> 4) + (cb & 15)) = w;
+            w.x = pack2_bf16(uv[0], uv[1]);
+            w.y = pack2_bf16(uv[2], uv[3]);
+            *reinterpret_cast<uint2 *>(smem + gstage_off(srow, (GROWB / 2 + cb) >> 4) +
+                                       (cb & 15)) = w;
+            w.x = pack2_bf16(hv[0], hv[1]);
+            w.y = pack2_bf16(hv[2], hv[3]);
+            *reinterpret_cast<uint2 *>(smem + H_BASE + stage_off(srow, cb >> 4) + (cb & 15)) = w;
+          }
+        }
+      }
+      __syncthreads();
+      // staged row r holds block row (r / 64) * 128 + 64 * pass + r % 64
+      constexpr int HALF = GCPR / 2;   // chunks per gate or up half row
+#pragma unroll 4
+      for (int idx = tid; idx < SR * GCPR; idx += 64 * NW) {
+        const int r = idx / GCPR, ch = idx % GCPR;
+        const int row = (r / 64) * 128 + 64 * pass + r % 64;
+        const int c = (ch % HALF) * 8;
+        if (row < nrows && c < ncols) {
+          const uint4 v = *reinterpret_cast<const uint4 *>(smem + gstage_off(r, ch));
+          *reinterpret_cast<uint4 *>(GU + (size_t)(tl.row0 + row) * (2 * Nout) +
+                                     (ch < HALF ? 0 : Nout) + n0 + c) = v;
+        }
+      }
+#pragma unroll 4
+      for (int idx = tid; idx < SR * CPR; idx += 64 * NW) {
+        const int r = idx / CPR, ch = idx % CPR;
+        const int row = (r / 64) * 128 + 64 * pass + r % 64;
+        if (row < nrows && ch * 8 < ncols) {
+          const uint4 v = *reinterpret_cast<const uint4 *>(smem + H_BASE + stage_off(r, ch));
+          *reinterpret_cast<uint4 *>(Out + (size_t)(tl.row0 + row) * Nout + n0 + ch * 8) = v;
+        }
+      }
+      __syncthreads();   // the stage is read out before the next pass reuses it
+    }
+    return;
+  }
 #pragma unroll
   for (int tm = 0; tm < P::TM; ++tm) {
     const int row = wm * 128 + tm * 32 + fr;
@@ -391,8 +477,7 @@ __device__ __forceinline__ void big_epilogue(
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
           if (GATE_UP) {
-            const float gv = acc[tm][tn][r], uv = acc[tm][tn + P::TN / 2][r];
-            v[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+            v[e] = swiglu(acc[tm][tn][r], acc[tm][tn + P::TN / 2][r]);
           } else {
             v[e] = acc[tm][tn][r];
           }
@@ -418,11 +503,13 @@ __device__ __forceinline__ void big_epilogue(
   }
 }
 
-template <bool GATE_UP, int BM, int BK, int NS, int NW>
+// SAVE (gate/up product only): also keep the pre-activation [G U] rows in GU
+// ([rows, 2 Nout], gate columns then up columns) for the backward.
+template <bool GATE_UP, bool SAVE, int BM, int BK, int NS, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
-    const int32_t *__restrict__ off, uint16_t *__restrict__ Out, int E_L, int Kdim,
-    int Nout, int n_tiles_n) {
+    const int32_t *__restrict__ off, uint16_t *__restrict__ Out, uint16_t *__restrict__ GU,
+    int E_L, int Kdim, int Nout, int n_tiles_n) {
   using P = BigTile<BM, BK, NS, NW>;
   // two A stages, NS B stages (NS = 3: the weight rows, which miss to HBM
   // more often, get two steps to land)
@@ -542,7 +629,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
 
   wait_vmcnt<0>();   // no direct load still in flight into the stages
   __syncthreads();   // every wave is done reading the last stage
-  big_epilogue<GATE_UP, BM, NW>(acc, smem, tl, Out, Nout, n0, wm, wn);
+  big_epilogue<GATE_UP, SAVE, BM, NW>(acc, smem, tl, Out, GU, Nout, n0, wm, wn);
 }
 
 // ------------------------------------------------------------------ fp32 SIMT
@@ -630,14 +717,19 @@ inline unsigned grid_blocks(const moe_shape_t &s, int bm, int n_tiles_n) {
 // register-staged kernel (any K % 8 == 0).
 template <bool GATE_UP>
 int launch_bf16(const moe_shape_t &s, const uint16_t *A, const uint16_t *W, const int32_t *off,
-                uint16_t *Out, int Kdim, int Nout, hipStream_t st) {
+                uint16_t *Out, int Kdim, int Nout, hipStream_t st, uint16_t *GU = nullptr) {
   const int E_L = s.N / s.ep_size;
   if (Kdim % 64 == 0) {
     constexpr int BM = 256;
     const int ntn = (int)ceil_div(Nout, GATE_UP ? 128 : 256);
-    hipLaunchKernelGGL((k_gemm_bf16_big<GATE_UP, BM, 64, MOE_BSTAGES, MOE_GEMM_WAVES>),
-                       dim3(grid_blocks(s, BM, ntn)), dim3(64 * MOE_GEMM_WAVES), 0, st, A, W, off,
-                       Out, E_L, Kdim, Nout, ntn);
+    if (GATE_UP && GU != nullptr)
+      hipLaunchKernelGGL((k_gemm_bf16_big<true, true, BM, 64, MOE_BSTAGES, MOE_GEMM_WAVES>),
+                         dim3(grid_blocks(s, BM, ntn)), dim3(64 * MOE_GEMM_WAVES), 0, st, A, W,
+                         off, Out, GU, E_L, Kdim, Nout, ntn);
+    else
+      hipLaunchKernelGGL((k_gemm_bf16_big<GATE_UP, false, BM, 64, MOE_BSTAGES, MOE_GEMM_WAVES>),
+                         dim3(grid_blocks(s, BM, ntn)), dim3(64 * MOE_GEMM_WAVES), 0, st, A, W,
+                         off, Out, nullptr, E_L, Kdim, Nout, ntn);
   } else {
     const int ntn = (int)ceil_div(Nout, GATE_UP ? kBW / 2 : kBW);
     hipLaunchKernelGGL(k_gemm_bf16<GATE_UP>, dim3(grid_blocks(s, kBM, ntn)), dim3(256), 0, st,
@@ -649,13 +741,19 @@ int launch_bf16(const moe_shape_t &s, const uint16_t *A, const uint16_t *W, cons
 }  // namespace
 
 int launch_expert_up(const moe_shape_t &s, const void *buf, const int32_t *offsets,
-                     const void *w_gu, void *h, hipStream_t st) {
+                     const void *w_gu, void *h, hipStream_t st, void *gu) {
   const int E_L = s.N / s.ep_size;
   const int32_t *off = offsets + (size_t)s.ep_rank * (E_L + 1);
+  if (gu != nullptr && !(s.dtype == MOE_BF16 && s.d % 64 == 0)) {
+    // kernels without a [G U] epilogue: the plain product, then the usual up
+    const int rc = launch_gemm_nt(s, buf, w_gu, off, gu, s.d, 2 * s.F, st);
+    if (rc != MOE_OK) return rc;
+    gu = nullptr;
+  }
   if (s.dtype == MOE_BF16)
     return launch_bf16<true>(s, static_cast<const uint16_t *>(buf),
                              static_cast<const uint16_t *>(w_gu), off, static_cast<uint16_t *>(h),
-                             s.d, s.F, st);
+                             s.d, s.F, st, static_cast<uint16_t *>(gu));
   const int ntn = (int)ceil_div(s.F, kFW / 2);
   hipLaunchKernelGGL(k_gemm_f32<true>, dim3(grid_blocks(s, kFM, ntn)), dim3(256), 0, st,
                      static_cast<const float *>(buf), static_cast<const float *>(w_gu), off,

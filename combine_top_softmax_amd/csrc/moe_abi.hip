@@ -112,6 +112,16 @@ int moe_expert_up(const moe_shape_t *shape, const void *buf, const int32_t *offs
   return moe::launch_expert_up(*shape, buf, offsets, w_gu, h, stream);
 }
 
+int moe_expert_up_save_gu(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
+                          const void *w_gu, void *h, void *gu, hipStream_t stream) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!aligned16(buf) || !aligned16(w_gu) || !aligned16(h) || !aligned16(gu) ||
+      !aligned4(offsets))
+    return MOE_EALIGN;
+  return moe::launch_expert_up(*shape, buf, offsets, w_gu, h, stream, gu);
+}
+
 int moe_expert_down(const moe_shape_t *shape, const void *h, const int32_t *offsets,
                     const void *w_down, void *y, hipStream_t stream) {
   const int rc = check_shape(shape);
@@ -165,6 +175,19 @@ int moe_expert_ffn_bwd_data(const moe_shape_t *shape, const void *buf, const int
     return MOE_EALIGN;
   return moe::launch_expert_ffn_bwd_data(*shape, buf, offsets, w_gu, w_down, dy, gu, dgu, dx_rows,
                                          stream);
+}
+
+int moe_expert_ffn_bwd_data_saved_gu(const moe_shape_t *shape, const int32_t *offsets,
+                                     const void *w_gu, const void *w_down, const void *dy,
+                                     const void *gu, void *dgu, void *dx_rows,
+                                     hipStream_t stream) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!aligned16(w_gu) || !aligned16(w_down) || !aligned16(dy) || !aligned16(gu) ||
+      !aligned16(dgu) || !aligned16(dx_rows) || !aligned4(offsets))
+    return MOE_EALIGN;
+  return moe::launch_expert_ffn_bwd_data_gu(*shape, offsets, w_gu, w_down, dy, gu, dgu, dx_rows,
+                                            stream);
 }
 
 int moe_expert_ffn_bwd_weight(const moe_shape_t *shape, const void *buf, const int32_t *offsets,

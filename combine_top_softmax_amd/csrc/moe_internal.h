@@ -29,8 +29,10 @@ int launch_dispatch(const moe_shape_t &s, const void *x, const int32_t *dest_ran
                     const int32_t *dest_row, void *buf, hipStream_t st);
 int launch_combine(const moe_shape_t &s, const void *y, const int32_t *dest_rank,
                    const int32_t *dest_row, const float *w, void *out, hipStream_t st);
+// gu != nullptr: also write the pre-activation [G U] rows ([rows, 2F]), equal
+// bit for bit to launch_gemm_nt(buf, w_gu) over the same rows.
 int launch_expert_up(const moe_shape_t &s, const void *buf, const int32_t *offsets,
-                     const void *w_gu, void *h, hipStream_t st);
+                     const void *w_gu, void *h, hipStream_t st, void *gu = nullptr);
 int launch_expert_down(const moe_shape_t &s, const void *h, const int32_t *offsets,
                        const void *w_d, void *y, hipStream_t st);
 // Out[r, :] = A[r] W[j]^T over the rows [off[j], off[j+1]) of each local expert
@@ -57,6 +59,10 @@ int launch_expert_down_mx(const moe_shape_t &s, const uint8_t *h_q, const uint8_
 int launch_expert_ffn_bwd_data(const moe_shape_t &s, const void *buf, const int32_t *offsets,
                                const void *w_gu, const void *w_down, const void *dy, void *gu,
                                void *dgu, void *dx_rows, hipStream_t st);
+// The data half from [G U] rows already in gu (no recompute).
+int launch_expert_ffn_bwd_data_gu(const moe_shape_t &s, const int32_t *offsets, const void *w_gu,
+                                  const void *w_down, const void *dy, const void *gu, void *dgu,
+                                  void *dx_rows, hipStream_t st);
 int launch_expert_ffn_bwd_weight(const moe_shape_t &s, const void *buf, const int32_t *offsets,
                                  const void *h, const void *dy, const void *dgu, float *dw_gu,
                                  float *dw_down, hipStream_t st);

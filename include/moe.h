@@ -159,6 +159,17 @@ int moe_expert_up(const moe_shape_t *shape, const void *buf, const int32_t *offs
 int moe_expert_down(const moe_shape_t *shape, const void *h, const int32_t *offsets,
                     const void *w_down, void *y, hipStream_t stream);
 
+/* Training forward of the up half: moe_expert_up, and in the same pass the
+ * pre-activation rows [G U] = X W_gu[j]^T that the expert backward reads
+ * (the [G U] of moe_expert_ffn_bwd), so that moe_expert_ffn_bwd_data_saved_gu
+ * can skip recomputing them. gu [E_L*C, 2F] in dtype, caller-owned: only the
+ * prefix rows are written, gate columns 0..F-1 then up columns F..2F-1, each
+ * value the fp32 accumulator rounded to nearest even. h is the same as
+ * moe_expert_up writes, and gu the same, bit for bit, as the recompute inside
+ * moe_expert_ffn_bwd_data writes for the same rows. */
+int moe_expert_up_save_gu(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
+                          const void *w_gu, void *h, void *gu, hipStream_t stream);
+
 /* Weighted combine (Olmo-core MoE report Sec. 5.6, Table 8, combine forward:
  * the token source pulls the selected expert rows and performs the
  * router-weighted reduction; invalid entries gather zero). For every token t:
@@ -230,6 +241,15 @@ int moe_expert_ffn_bwd_data(const moe_shape_t *shape, const void *buf, const int
 int moe_expert_ffn_bwd_weight(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
                               const void *h, const void *dy, const void *dgu, float *dw_gu,
                               float *dw_down, hipStream_t stream);
+
+/* moe_expert_ffn_bwd_data when the forward kept [G U] (moe_expert_up_save_gu):
+ * gu is read, not recomputed, so buf is not needed; dgu and dx_rows are
+ * written as by moe_expert_ffn_bwd_data, bit for bit. dgu may be the same
+ * buffer as gu (gu is then overwritten). */
+int moe_expert_ffn_bwd_data_saved_gu(const moe_shape_t *shape, const int32_t *offsets,
+                                     const void *w_gu, const void *w_down, const void *dy,
+                                     const void *gu, void *dgu, void *dx_rows,
+                                     hipStream_t stream);
 
 /* Dispatch backward (Table 8: each token pulls its route gradients and sums
  * them): dx[t] = sum over k ascending with dest_rank[t,k] == ep_rank of

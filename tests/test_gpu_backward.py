@@ -130,6 +130,60 @@ def test_expert_ffn_bwd_variants_agree(cfg):
             assert torch.equal(a, b)
 
 
+# bf16 with d % 64 != 0 takes the register-staged GEMM instead of the big-tile one
+SAVED_GU_CASES = SMALL + [SMALL[1].with_(name="small_d200_bf16", d=200, seed=41)]
+
+
+@pytest.mark.parametrize("cfg", SAVED_GU_CASES, ids=lambda c: c.name)
+def test_saved_gu_matches_recompute(cfg):
+    """moe_expert_up_save_gu writes the H of moe_expert_up and the [G U] that
+    the backward recompute writes, bit for bit, and nothing past the prefix;
+    moe_expert_ffn_bwd_data_saved_gu on it gives the recompute path's dgu and
+    dx_rows bit for bit (separate and in-place dgu); [G U] against the oracle."""
+    print(f"[case] saved gu {cfg.name}", flush=True)
+    inp = make_inputs(cfg, "cpu")
+    ref = oracle_route(cfg, inp.logits)
+    shape = moe.MoeShape.from_config(cfg)
+    dt = cfg.torch_dtype
+    rows, F, d = shape.rows, cfg.F, cfg.d
+    n = int(ref["offsets"][cfg.ep_rank, -1])
+    buf = random_rows(rows, d, dt, seed=cfg.seed + 610)
+    h_any = random_rows(rows, F, dt, seed=cfg.seed + 611)
+    dy = random_rows(rows, d, dt, seed=cfg.seed + 612)
+    off = _dev(ref["offsets"])
+    w_gu, w_d = inp.w_gu.cuda(), inp.w_d.cuda()
+    bufc, dyc = buf.cuda(), dy.cuda()
+
+    h_ref = poison_(torch.empty(rows, F, dtype=dt, device="cuda"))
+    moe.moe_expert_up(shape, bufc, off, w_gu, h_ref)
+    h = poison_(torch.empty(rows, F, dtype=dt, device="cuda"))
+    gu = poison_(torch.empty(rows, 2 * F, dtype=dt, device="cuda"))
+    moe.moe_expert_up_save_gu(shape, bufc, off, w_gu, h, gu)
+
+    gu_re = poison_(torch.empty(rows, 2 * F, dtype=dt, device="cuda"))
+    dgu_re = poison_(torch.empty(rows, 2 * F, dtype=dt, device="cuda"))
+    dx_re = poison_(torch.empty(rows, d, dtype=dt, device="cuda"))
+    moe.moe_expert_ffn_bwd_data(shape, bufc, off, w_gu, w_d, dyc, gu_re, dgu_re, dx_re)
+    dgu = poison_(torch.empty(rows, 2 * F, dtype=dt, device="cuda"))
+    dx = poison_(torch.empty(rows, d, dtype=dt, device="cuda"))
+    moe.moe_expert_ffn_bwd_data_saved_gu(shape, off, w_gu, w_d, dyc, gu, dgu, dx)
+    gu_in_place = gu.clone()
+    dx_ip = poison_(torch.empty(rows, d, dtype=dt, device="cuda"))
+    moe.moe_expert_ffn_bwd_data_saved_gu(shape, off, w_gu, w_d, dyc, gu_in_place, gu_in_place,
+                                         dx_ip)
+    torch.cuda.synchronize()
+    assert torch.equal(h[:n], h_ref[:n]), "H differs from moe_expert_up"
+    assert torch.equal(gu[:n], gu_re[:n]), "[G U] differs from the backward recompute"
+    for name, t in (("h", h), ("gu", gu), ("dgu", dgu), ("dx_rows", dx)):
+        assert bool(is_poison(t[n:]).all()), f"{name} tail written"
+    assert torch.equal(dgu[:n], dgu_re[:n]) and torch.equal(dx[:n], dx_re[:n])
+    assert torch.equal(gu_in_place[:n], dgu_re[:n]) and torch.equal(dx_ip[:n], dx_re[:n])
+    if n > 0:
+        r = orc.expert_ffn_bwd(_f64(buf), ref["offsets"][cfg.ep_rank], _f64(inp.w_gu),
+                               _f64(inp.w_d), _f64(h_any), _f64(dy), cfg.dtype)
+        assert_rows_close(to_np(gu[:n]), r["gu"][:n], tol_of(cfg.dtype), "gu")
+
+
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_dispatch_bwd_matches_oracle(cfg):
     inp = make_inputs(cfg, "cpu", with_weights=False)
@@ -238,6 +292,33 @@ def test_backward_shards_sum_to_unsharded_on_gpu():
 
 
 FULL = ["tiny_f32", "olmoe_bf16", "gptoss_shard_bf16", "zipf_skew_bf16", "finegrained_shard_bf16"]
+
+
+@pytest.mark.parametrize("name", ["olmoe_bf16", "gptoss_shard_bf16"])
+def test_full_config_saved_gu_layer(name):
+    """Full workload sizes: MoELayer.forward(save_gu=True) + backward gives the
+    outputs and every gradient of forward + backward with the recompute, bit
+    for bit (the oracle check of that path is test_full_config_backward)."""
+    from combine_top_softmax_amd.workloads import CONFIGS
+    cfg = CONFIGS[name]
+    print(f"[case] full saved gu {name}", flush=True)
+    inp = make_inputs(cfg, "cuda")
+    dout = random_rows(cfg.T, cfg.d, cfg.torch_dtype, seed=cfg.seed + 900).cuda()
+    layer = moe.MoELayer(moe.MoeShape.from_config(cfg), "cuda")
+    got = []
+    for save in (False, True):
+        out = layer.forward(inp.logits, inp.x, inp.w_gu, inp.w_d, save_gu=save).clone()
+        h = layer.h.clone()
+        grads = [t.clone() for t in layer.backward(dout, inp.w_gu, inp.w_d)]
+        got.append([out, h, layer.dw.clone(), layer.dx_rows.clone()] + grads)
+        assert not layer.gu_saved
+    torch.cuda.synchronize()
+    n = int(layer.route.offsets[cfg.ep_rank, -1])
+    names = ["out", "h", "dw", "dx_rows", "dx", "dlogits", "dw_gu", "dw_down"]
+    for nm, a, b in zip(names, *got):
+        if nm in ("h", "dx_rows"):
+            a, b = a[:n], b[:n]
+        assert torch.equal(a, b), f"{nm} differs with the saved [G U]"
 
 
 @pytest.mark.parametrize("name", FULL)
