@@ -53,7 +53,11 @@ class MoeShape:
 
     @property
     def rows(self) -> int:
-        return self.E_L * self.capacity
+        """Rows of the capacity-shaped buffers (moe_buffer_rows)."""
+        r = _abi.load().moe_buffer_rows(ctypes.byref(self.c()))
+        if r < 0:
+            _abi.check("moe_buffer_rows", int(r))
+        return int(r)
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -98,7 +102,7 @@ class RouteOut:
     drop_mask: torch.Tensor  # [T,K] uint8
     counts: torch.Tensor     # [N] int32
     offsets: torch.Tensor    # [ep_size, E_L+1] int32
-    row_src: torch.Tensor | None  # [E_L*C] int32
+    row_src: torch.Tensor | None  # [rows] int32
 
     @classmethod
     def empty(cls, shape: MoeShape, device="cuda", row_src: bool = True) -> "RouteOut":

@@ -41,6 +41,7 @@ SIGNATURES = {
     "moe_route_map": (ctypes.c_int, [_SHAPE, _P, _ROUTE, _P, ctypes.c_size_t, _P]),
     "moe_dispatch_rows": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_expert_ffn": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_buffer_rows": (ctypes.c_int64, [_SHAPE]),
     "moe_expert_up": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_expert_up_save_gu": (ctypes.c_int, [_SHAPE] + [_P] * 6),
     "moe_expert_down": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),

@@ -866,7 +866,7 @@ inline dim3 gemm_grid(int mode, const moe_shape_t &s, int tile, const GemmArgs &
   if (mode == BW_WG)
     tiles = (int64_t)E_L * p.m_tiles * p.n_tiles_n;
   else
-    tiles = (ceil_div((int64_t)E_L * s.capacity, tile) + E_L) * p.n_tiles_n;
+    tiles = (ceil_div(buffer_rows(s), tile) + E_L) * p.n_tiles_n;
   return dim3((unsigned)(ceil_div(tiles, kNumXcd) * kNumXcd));
 }
 

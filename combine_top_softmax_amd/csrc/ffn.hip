@@ -16,7 +16,7 @@
 // the [out, in] weight rows), so each lane loads 16-byte runs along K.
 //
 // Scheduling from device offsets: the grid is sized from the capacity bound
-// (sum_j ceil(n_j/BM) <= ceil(E_L*C/BM) + E_L m-tiles); every block recomputes
+// (sum_j ceil(n_j/BM) <= ceil(R/BM) + E_L m-tiles, R the buffer rows); every block recomputes
 // the per-expert m-tile counts from the offsets with a wave scan, maps its
 // block id to a real tile and exits if there is none. The block id -> tile map
 // is XCD-aware: blocks are dealt to the 8 XCDs round-robin, so block b gets
@@ -707,7 +707,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(
 // Grid: every possible m-tile times the n-tiles, rounded up to the XCD count.
 inline unsigned grid_blocks(const moe_shape_t &s, int bm, int n_tiles_n) {
   const int E_L = s.N / s.ep_size;
-  const int64_t max_m = ceil_div((int64_t)E_L * s.capacity, bm) + E_L;
+  const int64_t max_m = ceil_div(buffer_rows(s), bm) + E_L;
   return (unsigned)(ceil_div(max_m * n_tiles_n, kNumXcd) * kNumXcd);
 }
 

@@ -22,9 +22,9 @@ int check_shape(const moe_shape_t *s) {
   if (s->K > s->N || s->K > MOE_MAX_K || s->N > MOE_MAX_EXPERTS) return MOE_EINVAL;
   if (s->N % s->ep_size != 0 || s->ep_rank < 0 || s->ep_rank >= s->ep_size) return MOE_EINVAL;
   if (s->d % 8 != 0 || s->F % 8 != 0) return MOE_EINVAL;
-  const int64_t E_L = s->N / s->ep_size;
+  // the buffer rows, the offsets and every row index stay below T*K (or
+  // min(K, E_L) for an empty batch), whatever the capacity
   if ((int64_t)s->T * s->K >= (int64_t)1 << 31) return MOE_EINVAL;
-  if (E_L * s->capacity >= (int64_t)1 << 31) return MOE_EINVAL;
   return MOE_OK;
 }
 
@@ -52,6 +52,11 @@ int check_route_out(const moe_shape_t &s, const moe_route_out_t *o, bool need_to
 extern "C" {
 
 int moe_validate_shape(const moe_shape_t *shape) { return check_shape(shape); }
+
+int64_t moe_buffer_rows(const moe_shape_t *shape) {
+  const int rc = check_shape(shape);
+  return rc != MOE_OK ? rc : moe::buffer_rows(*shape);
+}
 
 const char *moe_strerror(int code) {
   switch (code) {

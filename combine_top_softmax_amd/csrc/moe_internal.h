@@ -21,6 +21,15 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int route_tiles(const moe_shape_t &s) {
   return s.T > 0 ? (int)ceil_div(s.T, kRouteTile) : 1;
 }
+// Rows of every capacity-shaped buffer (moe_buffer_rows): the kept local
+// routes never exceed E_L*C, nor max(T,1)*min(K, E_L) (a token's K experts
+// are distinct, so at most min(K, E_L) of its routes are local).
+inline int64_t buffer_rows(const moe_shape_t &s) {
+  const int64_t E_L = s.N / s.ep_size;
+  const int64_t per_tok = s.K < E_L ? s.K : E_L;
+  const int64_t by_tok = (int64_t)(s.T > 0 ? s.T : 1) * per_tok;
+  return E_L * s.capacity < by_tok ? E_L * s.capacity : by_tok;
+}
 
 // Launchers (return MOE_OK or MOE_EHIP). Shapes are already validated.
 int launch_route(const moe_shape_t &s, const float *logits, const int32_t *ids_in,

@@ -469,7 +469,7 @@ __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
 
 inline unsigned mx_grid(const moe_shape_t &s, int ntn) {
   const int E_L = s.N / s.ep_size;
-  const int64_t max_m = ceil_div((int64_t)E_L * s.capacity, mxg::BM) + E_L;
+  const int64_t max_m = ceil_div(buffer_rows(s), mxg::BM) + E_L;
   return (unsigned)(ceil_div(max_m * ntn, kNumXcd) * kNumXcd);
 }
 

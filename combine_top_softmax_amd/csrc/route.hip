@@ -313,7 +313,7 @@ __global__ __launch_bounds__(64) void k_assign(
     int32_t *__restrict__ dest_rank, int32_t *__restrict__ dest_row,
     uint8_t *__restrict__ drop_mask, int32_t *__restrict__ offsets,
     int32_t *__restrict__ row_src, int T, int N, int K, int C, int E_L, int ep_size,
-    int ep_rank, int ntiles) {
+    int ep_rank, int ntiles, int rows) {
   __shared__ int s_g[MOE_MAX_EXPERTS + 1];  // exclusive scan of min(counts, C)
   const int lane = threadIdx.x;
   const int tile = blockIdx.x;
@@ -383,9 +383,7 @@ __global__ __launch_bounds__(64) void k_assign(
   }
   if (row_src != nullptr) {
     const int used = s_g[(ep_rank + 1) * E_L] - s_g[ep_rank * E_L];
-    const int64_t rows = (int64_t)E_L * C;
-    for (int64_t r = used + (int64_t)tile * kWave + lane; r < rows; r += (int64_t)ntiles * kWave)
-      row_src[r] = -1;
+    for (int r = used + tile * kWave + lane; r < rows; r += ntiles * kWave) row_src[r] = -1;
   }
 }
 
@@ -407,7 +405,7 @@ int launch_route_km(const moe_shape_t &s, const float *logits, const int32_t *id
   const int E_L = s.N / s.ep_size;
   hipLaunchKernelGGL((k_assign<KM>), dim3(ntiles), dim3(64), 0, st, ids, hist, rank_ws, o.counts,
                      o.dest_rank, o.dest_row, o.drop_mask, o.offsets, o.row_src, s.T, s.N,
-                     s.K, s.capacity, E_L, s.ep_size, s.ep_rank, ntiles);
+                     s.K, s.capacity, E_L, s.ep_size, s.ep_rank, ntiles, (int)buffer_rows(s));
   return launch_status();
 }
 

@@ -16,7 +16,9 @@ Recipe (one per named workload):
     rounds once to fp32 (the router GEMM sits upstream of the layer boundary,
     so it is part of input synthesis). The larger layers use i.i.d. N(0, 1)
     logits; the skewed layer adds a per-expert Zipf(s) bias (e + 1)^(-s).
-  * capacity C = ceil(T * K * cf / N) in exact rational arithmetic.
+  * capacity C = ceil(T * K * cf / N) in exact rational arithmetic; a dropless
+    workload takes C = max(T, 1) instead (no expert can receive more than T
+    routes, so none is dropped), with buffers of the upper-bound row count.
 
 The shapes follow the pages' workloads: an OLMoE-like layer (64 experts, top-8),
 a GPT-OSS-20B-like layer seen from one shard of an 8-way expert split (32
@@ -48,9 +50,12 @@ class LayerConfig:
     logits: str = "gauss"   # "router" | "gauss" | "zipf"
     zipf_s: float = 1.1
     seed: int = 0
+    dropless: bool = False  # capacity = T: every route kept (cf unused)
 
     @property
     def capacity(self) -> int:
+        if self.dropless:
+            return max(self.T, 1)
         return math.ceil(Fraction(self.T * self.K, self.N) * self.cf)
 
     @property
@@ -82,6 +87,10 @@ CONFIGS = {
     "finegrained_shard_bf16": LayerConfig("finegrained_shard_bf16", T=65536, d=4096, N=256,
                                           K=8, F=2048, cf=Fraction(3, 2), dtype="bf16",
                                           ep_size=8, ep_rank=0, seed=5),
+    # the skewed layer's inputs, routed dropless into upper-bound buffers
+    "zipf_dropless_bf16": LayerConfig("zipf_dropless_bf16", T=32768, d=4096, N=128, K=8,
+                                      F=1536, cf=Fraction(1), dtype="bf16", logits="zipf",
+                                      seed=4, dropless=True),
 }
 
 

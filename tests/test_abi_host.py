@@ -119,3 +119,39 @@ def test_backward_halves_validate_on_the_host():
     bad = moe.MoeShape(**{**BASE, "F": 12}).c()
     assert lib.moe_expert_ffn_bwd_data(ctypes.byref(bad), *([16] * 8), None) == _abi.MOE_EINVAL
     assert lib.moe_expert_ffn_bwd_weight(ctypes.byref(bad), *([16] * 7), None) == _abi.MOE_EINVAL
+
+
+def test_buffer_rows_bound_the_oracle_prefix():
+    """moe_buffer_rows never cuts the packed prefix the oracle's route map
+    fills (the kept local routes), and it is reached when every route is
+    local and kept (dropless, one rank) or every expert is overfull."""
+    import numpy as np
+    from combine_top_softmax_amd.workloads import random_ids
+    from oracle import moe_oracle as orc
+    cases = [(300, 16, 4, 1, 0, 300), (300, 16, 4, 4, 2, 300), (300, 16, 4, 4, 3, 20),
+             (257, 5, 5, 1, 0, 7), (64, 64, 8, 8, 7, 64), (1, 4, 2, 2, 1, 1)]
+    for T, N, K, ep, r, C in cases:
+        ids = random_ids(T, N, K, seed=T + N + C).numpy()
+        s = moe.MoeShape(T=T, d=8, N=N, K=K, F=8, ep_size=ep, ep_rank=r, capacity=C, dtype="f32")
+        kept = int(orc.route_map(ids, N, ep, C, r)["offsets"][r, -1])
+        assert kept <= s.rows, (T, N, K, ep, r, C)
+    # dropless on one rank: every route kept, the bound T*K reached exactly
+    ids = random_ids(200, 8, 3, seed=5).numpy()
+    s = moe.MoeShape(T=200, d=8, N=8, K=3, F=8, ep_size=1, ep_rank=0, capacity=200, dtype="f32")
+    rm = orc.route_map(ids, 8, 1, 200, 0)
+    assert int(rm["drop_mask"].sum()) == 0 and int(rm["offsets"][0, -1]) == s.rows == 600
+    # one-row capacity with every expert over it: the envelope E_L*C reached
+    s = moe.MoeShape(T=200, d=8, N=8, K=3, F=8, ep_size=2, ep_rank=1, capacity=1, dtype="f32")
+    assert int(orc.route_map(ids, 8, 2, 1, 1)["offsets"][1, -1]) == s.rows == 4
+
+
+def test_buffer_rows_of_special_shapes():
+    lib = _abi.load()
+    # an empty batch keeps one-row buffers; a capacity past 2^31 / E_L is valid
+    assert moe.MoeShape(**{**BASE, "T": 0}).rows == 2
+    big = moe.MoeShape(**{**BASE, "capacity": (1 << 31) - 1})
+    assert moe.moe_validate_shape(big) == 0 and big.rows == 64 * 2
+    cs = moe.MoeShape(**{**BASE, "K": 0}).c()
+    assert lib.moe_buffer_rows(ctypes.byref(cs)) == _abi.MOE_EINVAL
+    with pytest.raises(moe.MoeError):
+        moe.MoeShape(**{**BASE, "K": 0}).rows

@@ -291,7 +291,8 @@ def test_backward_shards_sum_to_unsharded_on_gpu():
     np.testing.assert_allclose(dl.cpu().numpy(), fdl, rtol=1e-5, atol=1e-6 * np.abs(fdl).max())
 
 
-FULL = ["tiny_f32", "olmoe_bf16", "gptoss_shard_bf16", "zipf_skew_bf16", "finegrained_shard_bf16"]
+FULL = ["tiny_f32", "olmoe_bf16", "gptoss_shard_bf16", "zipf_skew_bf16", "finegrained_shard_bf16",
+        "zipf_dropless_bf16"]
 
 
 @pytest.mark.parametrize("name", ["olmoe_bf16", "gptoss_shard_bf16"])

@@ -11,8 +11,8 @@ import torch
 import combine_top_softmax_amd as moe
 from combine_top_softmax_amd.workloads import LayerConfig, make_inputs, random_ids
 from oracle import moe_oracle as orc
-from gpu_util import (assert_rows_close, check_route, is_poison, oracle_route, poison_,
-                      route_gpu, to_np, tol_of)
+from gpu_util import (assert_route_fields, assert_row_src, assert_rows_close, check_route,
+                      is_poison, oracle_route, poison_, route_gpu, to_np, tol_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -112,8 +112,8 @@ def test_route_map_maximum_sizes_with_invalid():
     moe.moe_route_map(shape, ids.cuda(), out, ws)
     ref = orc.route_map(ids.numpy(), N, ep, C, 5)
     torch.cuda.synchronize()
-    for k in ("counts", "offsets", "dest_rank", "dest_row", "drop_mask", "row_src"):
-        np.testing.assert_array_equal(to_np(getattr(out, k)), ref[k], err_msg=k)
+    assert_route_fields(out, ref, ("counts", "offsets", "dest_rank", "dest_row", "drop_mask",
+                                   "row_src"))
 
 
 def test_route_map_long_batch_tile_scan_past_register_run():
@@ -128,8 +128,8 @@ def test_route_map_long_batch_tile_scan_past_register_run():
     moe.moe_route_map(shape, ids.cuda(), out, ws)
     ref = orc.route_map(ids.numpy(), N, ep, C, 1)
     torch.cuda.synchronize()
-    for k in ("counts", "offsets", "dest_rank", "dest_row", "drop_mask", "row_src"):
-        np.testing.assert_array_equal(to_np(getattr(out, k)), ref[k], err_msg=k)
+    assert_route_fields(out, ref, ("counts", "offsets", "dest_rank", "dest_row", "drop_mask",
+                                   "row_src"))
 
 
 def test_wide_rows_span_several_row_passes():

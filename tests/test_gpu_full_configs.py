@@ -17,7 +17,8 @@ from gpu_util import assert_rows_close, check_route, oracle_route, poison_, to_n
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["tiny_f32", "olmoe_bf16", "gptoss_shard_bf16", "zipf_skew_bf16", "finegrained_shard_bf16"]
+FULL = ["tiny_f32", "olmoe_bf16", "gptoss_shard_bf16", "zipf_skew_bf16", "finegrained_shard_bf16",
+        "zipf_dropless_bf16"]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -35,6 +35,8 @@ MX_SMALL = [
                 logits="zipf", zipf_s=1.1, seed=43),
     LayerConfig("mx_many_experts", T=300, d=128, N=320, K=8, F=128, cf=Fraction(2),
                 dtype="bf16", ep_size=2, ep_rank=1, seed=44),
+    LayerConfig("mx_zipf_dropless", T=1500, d=128, N=24, K=3, F=128, cf=Fraction(1),
+                dtype="bf16", logits="zipf", zipf_s=1.1, seed=43, dropless=True),
 ]
 
 
@@ -180,7 +182,8 @@ def test_expert_up_down_mx_stages(cfg):
 # median by orders of magnitude, isolated flips move single rows).
 E2E_ROW, E2E_MEDIAN = 5e-2, 1e-2
 MX_LAYER = MX_SMALL[:2] + [MX_SMALL[2].with_(name="mx_zipf_drops_256", d=256, F=256),
-                           MX_SMALL[3].with_(name="mx_many_experts_256", d=256, F=256)]
+                           MX_SMALL[3].with_(name="mx_many_experts_256", d=256, F=256),
+                           MX_SMALL[4].with_(name="mx_zipf_dropless_256", d=256, F=256)]
 
 
 def _check_e2e(got, ref, what):
@@ -221,7 +224,8 @@ def test_layer_mx_matches_oracle(cfg):
     _check_e2e(to_np(layer.out), ref["out"], "out")
 
 
-@pytest.mark.parametrize("name", ["olmoe_bf16", "zipf_skew_bf16", "finegrained_shard_bf16"])
+@pytest.mark.parametrize("name", ["olmoe_bf16", "zipf_skew_bf16", "finegrained_shard_bf16",
+                                  "zipf_dropless_bf16"])
 def test_full_config_mx(name):
     """Full workload sizes: MoELayer.forward_mx; routing and quantize-on-dispatch
     checked on sampled rows bit-exactly, the expert outputs of sampled rows of

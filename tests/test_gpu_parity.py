@@ -16,8 +16,8 @@ import torch
 import combine_top_softmax_amd as moe
 from combine_top_softmax_amd.workloads import LayerConfig, CONFIGS, make_inputs, random_rows, random_ids
 from oracle import moe_oracle as orc
-from gpu_util import (assert_rows_close, check_route, is_poison, oracle_route, poison_,
-                      route_gpu, to_np, tol_of)
+from gpu_util import (assert_route_fields, assert_row_src, assert_rows_close, check_route,
+                      is_poison, oracle_route, poison_, route_gpu, to_np, tol_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +37,12 @@ SMALL = [
                 dtype="bf16", ep_size=8, ep_rank=5, seed=16),
     LayerConfig("many_experts_bf16", T=300, d=64, N=320, K=8, F=64, cf=Fraction(2),
                 dtype="bf16", ep_size=2, ep_rank=1, seed=17),
+    # dropless (capacity T, upper-bound buffers) on skewed routing
+    LayerConfig("small_zipf_dropless_bf16", T=1500, d=128, N=24, K=3, F=136, cf=Fraction(1),
+                dtype="bf16", logits="zipf", zipf_s=1.1, seed=13, dropless=True),
+    LayerConfig("dropless_shard_zipf_bf16", T=777, d=384, N=32, K=4, F=256, cf=Fraction(1),
+                dtype="bf16", ep_size=4, ep_rank=0, logits="zipf", zipf_s=1.1, seed=18,
+                dropless=True),
 ]
 
 
@@ -84,6 +90,37 @@ def test_layer_stages_match_oracle(cfg):
     assert_rows_close(to_np(layer.out), ref["out"], tol, "out")
 
 
+@pytest.mark.parametrize("cfg", [c for c in SMALL if c.dropless], ids=lambda c: c.name)
+def test_dropless_keeps_every_route(cfg):
+    """Dropless mode (capacity T, upper-bound buffers of moe_buffer_rows rows):
+    on skewed routing that drops routes at capacity factor 1, every local
+    route is kept and packed, and the buffers are smaller than the E_L*C
+    envelope. Sync-free: the whole layer runs with host syncs forbidden."""
+    print(f"[case] dropless {cfg.name}", flush=True)
+    inp = make_inputs(cfg, "cpu")
+    capped = cfg.with_(dropless=False)
+    assert int(oracle_route(capped, inp.logits)["drop_mask"].sum()) > 0
+    shape = moe.MoeShape.from_config(cfg)
+    assert shape.rows == cfg.T * min(cfg.K, cfg.E_L) < cfg.E_L * cfg.capacity
+    layer = moe.MoELayer(shape, "cuda")
+    dev = _to_dev(inp)
+    torch.cuda.synchronize()
+    torch.cuda.set_sync_debug_mode("error")
+    try:
+        layer.forward(dev.logits, dev.x, dev.w_gu, dev.w_d)
+    finally:
+        torch.cuda.set_sync_debug_mode(0)
+    torch.cuda.synchronize()
+    idx = to_np(layer.route.topk_idx)
+    local = (idx // cfg.E_L) == cfg.ep_rank
+    assert int(to_np(layer.route.drop_mask).sum()) == 0
+    assert np.array_equal(to_np(layer.route.dest_rank) >= 0, np.ones_like(local))
+    n = int(to_np(layer.route.offsets)[cfg.ep_rank, -1])
+    assert n == int(local.sum())
+    rows = to_np(layer.route.dest_row)[local]
+    assert np.array_equal(np.sort(rows), np.arange(n))   # a permutation of the prefix
+
+
 @pytest.mark.parametrize("cfg", SMALL[:4], ids=lambda c: c.name)
 def test_combine_alone_matches_oracle(cfg):
     """Combine on stand-in expert rows (seeded, not computed by the HIP path)."""
@@ -116,7 +153,7 @@ def test_route_map_fig16_on_gpu(golden_dir):
         assert to_np(out.dest_row).tolist() == g["dest_row"]
         assert int(to_np(out.offsets)[0, -1]) == g["rank0_rows_used"]
         ref = orc.route_map(ids.numpy(), 4, 2, g["capacity_min"], ep_rank)
-        np.testing.assert_array_equal(to_np(out.row_src), ref["row_src"])
+        assert_row_src(to_np(out.row_src), ref["row_src"])
         np.testing.assert_array_equal(to_np(out.drop_mask), ref["drop_mask"])
 
 
@@ -133,8 +170,8 @@ def test_route_map_random_ids_with_invalid(T, N, K, C, ep, frac):
         ref = orc.route_map(ids.numpy(), N, ep, C, ep_rank)
         ref["topk_idx"] = ids.numpy()
         torch.cuda.synchronize()
-        for k in ("counts", "offsets", "dest_rank", "dest_row", "drop_mask", "row_src"):
-            np.testing.assert_array_equal(to_np(getattr(out, k)), ref[k], err_msg=k)
+        assert_route_fields(out, ref, ("counts", "offsets", "dest_rank", "dest_row",
+                                       "drop_mask", "row_src"))
 
 
 @pytest.mark.parametrize("case", ["single_token", "one_expert", "constant_logits", "capacity_one"])
