@@ -41,7 +41,9 @@ design notes of the repository):
   * gating: softmax over the K selected logits (every printed weight set sums
     to one and is in descending order);
   * ties in top-K: lower expert id first; -0.0 equals +0.0;
-  * capacity is per expert, C = ceil(T*K*cf/N); the first C routes of an expert
+  * capacity is per expert and an input here (the workloads take
+    C = ceil(T*K*cf/N), or C = T for the dropless mode, where no expert can
+    receive more than C routes and none is dropped); the first C routes of an expert
     in token order are kept, later ones dropped -- this admission order is
     PARITY UNPINNED by the pages (the drawing's single drop cannot come from
     any per-expert token-order rule); it is pinned only by brute force of the
