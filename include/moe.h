@@ -68,7 +68,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
  * N <= MOE_MAX_EXPERTS, N % ep_size == 0, 0 <= ep_rank < ep_size, d and F
  * multiples of 8, T*K < 2^31. Any capacity C >= 1 is valid; C >= T keeps
  * every route (no expert can receive more than T routes): the dropless mode,
- * with buffers of the upper-bound size R below and no host-visible count.
+ * with buffers of the upper-bound size Rmax below and no host-visible count.
  * An empty batch (T == 0) is valid: moe_route / moe_route_map write zero
  * counts and offsets and a row_src of -1 (their [T,K] pointers may be NULL),
  * moe_expert_ffn finds no row, and moe_dispatch_rows / moe_combine return
@@ -78,9 +78,9 @@ typedef struct {
   moe_dtype_t dtype;
 } moe_shape_t;
 
-/* Rows R of every capacity-shaped buffer of a rank (buf, h, y, gu, dgu, dy,
- * dx_rows, row_src and the MXFP8 qbuf, sbuf, h_q, h_s; "[R, ...]" below):
- *   R = min(E_L*C, max(T,1) * min(K, E_L)),
+/* Rows Rmax of every capacity-shaped buffer of a rank (buf, h, y, gu, dgu, dy,
+ * dx_rows, row_src and the MXFP8 qbuf, sbuf, h_q, h_s; "[Rmax, ...]" below):
+ *   Rmax = min(E_L*C, max(T,1) * min(K, E_L)),
  * the most kept local routes there can be: each local expert keeps at most C,
  * and a token's K experts are distinct, so at most min(K, E_L) of its routes
  * are local (max(T,1): an empty batch still gets one-row buffers). Only the
@@ -90,7 +90,7 @@ typedef struct {
  * Different Trade-offs, Sec. 23.3: dispatch into preallocated upper-bound
  * buffers with device-side grouped GEMM instead of a host sync on counts);
  * with a smaller C it is the fixed capacity envelope of Sec. 8.5 (report
- * Section 08), which may drop routes. Returns R, or a negative MOE_E* code
+ * Section 08), which may drop routes. Returns Rmax, or a negative MOE_E* code
  * for an invalid shape. */
 int64_t moe_buffer_rows(const moe_shape_t *shape);
 
@@ -104,7 +104,7 @@ int64_t moe_buffer_rows(const moe_shape_t *shape);
  *   offsets   [ep_size*(E_L+1)] int32  per rank r, entry r*(E_L+1)+j is the
  *             number of kept rows of r's local experts j' < j (j = 0..E_L):
  *             the cumulative offsets the grouped FFN consumes
- *   row_src   [R] int32 or NULL   for rank ep_rank: t*K+k of the route
+ *   row_src   [Rmax] int32 or NULL   for rank ep_rank: t*K+k of the route
  *             stored in each row, -1 on every row after the packed prefix
  * Olmo-core MoE report Sec. 5.4: two [T,K] tensors give destination rank and
  * destination row, negative entries mark invalid or capacity-dropped routes;
@@ -149,7 +149,7 @@ int moe_route_map(const moe_shape_t *shape, const int32_t *topk_idx_in,
 /* Rowwise dispatch (Olmo-core MoE report Sec. 5.6, Table 8, dispatch forward:
  * the token source pushes x_t to the capacity row of the selected expert;
  * negative destinations are skipped). buf[dest_row[t,k]] = x[t] for every
- * route with dest_rank[t,k] == ep_rank. x [T,d], buf [R, d] in dtype.
+ * route with dest_rank[t,k] == ep_rank. x [T,d], buf [Rmax, d] in dtype.
  * Rows of buf after the packed prefix are neither read nor written. */
 int moe_dispatch_rows(const moe_shape_t *shape, const void *x, const int32_t *dest_rank,
                       const int32_t *dest_row, void *buf, hipStream_t stream);
@@ -161,8 +161,8 @@ int moe_dispatch_rows(const moe_shape_t *shape, const void *x, const int32_t *de
  * o = offsets + ep_rank*(E_L+1):
  *   G = X W_gu[j][0:F]^T,  U = X W_gu[j][F:2F]^T,  H = silu(G) * U,
  *   Y = H W_d[j]^T
- * buf [R, d], w_gu [E_L, 2F, d] (rows 0..F-1 gate, F..2F-1 up),
- * w_down [E_L, d, F], h [R, F] (caller-owned scratch), y [R, d];
+ * buf [Rmax, d], w_gu [E_L, 2F, d] (rows 0..F-1 gate, F..2F-1 up),
+ * w_down [E_L, d, F], h [Rmax, F] (caller-owned scratch), y [Rmax, d];
  * all in dtype. Accumulation is fp32; H and Y are stored in dtype with
  * round-to-nearest-even. Only prefix rows of h and y are written. */
 int moe_expert_ffn(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
@@ -180,7 +180,7 @@ int moe_expert_down(const moe_shape_t *shape, const void *h, const int32_t *offs
 /* Training forward of the up half: moe_expert_up, and in the same pass the
  * pre-activation rows [G U] = X W_gu[j]^T that the expert backward reads
  * (the [G U] of moe_expert_ffn_bwd), so that moe_expert_ffn_bwd_data_saved_gu
- * can skip recomputing them. gu [R, 2F] in dtype, caller-owned: only the
+ * can skip recomputing them. gu [Rmax, 2F] in dtype, caller-owned: only the
  * prefix rows are written, gate columns 0..F-1 then up columns F..2F-1, each
  * value the fp32 accumulator rounded to nearest even. h is the same as
  * moe_expert_up writes, and gu the same, bit for bit, as the recompute inside
@@ -196,7 +196,7 @@ int moe_expert_up_save_gu(const moe_shape_t *shape, const void *buf, const int32
  * accumulated in fp32 and stored in dtype; a token with no kept local route
  * gets an exact zero row. On an expert shard this is the shard's partial
  * output; the sum over all ranks is the full layer output (AWS Neuron EP
- * design, "Why a single all-reduce works"). y [R, d], out [T,d]. */
+ * design, "Why a single all-reduce works"). y [Rmax, d], out [T,d]. */
 int moe_combine(const moe_shape_t *shape, const void *y, const int32_t *dest_rank,
                 const int32_t *dest_row, const float *topk_w, void *out,
                 hipStream_t stream);
@@ -218,11 +218,11 @@ int moe_combine(const moe_shape_t *shape, const void *y, const int32_t *dest_ran
 /* Combine backward (Table 8: the weighted output gradient is pushed to each
  * accepted route's expert-output row; the router-weight gradient uses the
  * gathered expert output with the same token's output gradient).
- * dout [T,d] and y [R,d] (the forward's expert outputs) in dtype,
+ * dout [T,d] and y [Rmax,d] (the forward's expert outputs) in dtype,
  * topk_w [T,K] fp32. For every route with dest_rank[t,k] == ep_rank:
  *   dy[dest_row[t,k]] = topk_w[t,k] * dout[t]      (stored in dtype)
  *   dw[t,k]           = <dout[t], y[dest_row[t,k]]> (fp32 accumulation)
- * every other route gets dw[t,k] = 0. dy [R,d]: exactly the packed prefix
+ * every other route gets dw[t,k] = 0. dy [Rmax,d]: exactly the packed prefix
  * rows are written; dw [T,K] fp32 is fully written. T == 0: MOE_OK, nothing
  * touched. */
 int moe_combine_bwd(const moe_shape_t *shape, const void *dout, const void *y,
@@ -237,7 +237,7 @@ int moe_combine_bwd(const moe_shape_t *shape, const void *dout, const void *y,
  *   dG = dH * U * s * (1 + G*(1 - s)),  dU = dH * G * s   stored in dgu = [dG dU]
  *   dx_rows = [dG dU] W_gu[j]
  *   dw_down[j] = dY^T H,  dw_gu[j] = [dG dU]^T X     (fp32)
- * gu, dgu [R, 2F] and dx_rows [R, d] in dtype: caller-owned, only the
+ * gu, dgu [Rmax, 2F] and dx_rows [Rmax, d] in dtype: caller-owned, only the
  * prefix rows are written; dgu may be the same buffer as gu (gu is then
  * overwritten). Accumulation is fp32; row results are stored in dtype with
  * round-to-nearest-even. dw_gu [E_L,2F,d] and dw_down [E_L,d,F] fp32 are fully
@@ -272,7 +272,7 @@ int moe_expert_ffn_bwd_data_saved_gu(const moe_shape_t *shape, const int32_t *of
 /* Dispatch backward (Table 8: each token pulls its route gradients and sums
  * them): dx[t] = sum over k ascending with dest_rank[t,k] == ep_rank of
  * dx_rows[dest_row[t,k]], accumulated in fp32 and stored in dtype; a token
- * with no kept local route gets an exact zero row. dx_rows [R,d],
+ * with no kept local route gets an exact zero row. dx_rows [Rmax,d],
  * dx [T,d]. T == 0: MOE_OK, nothing touched. */
 int moe_dispatch_bwd(const moe_shape_t *shape, const void *dx_rows, const int32_t *dest_rank,
                      const int32_t *dest_row, void *dx, hipStream_t stream);
@@ -314,7 +314,7 @@ int moe_mx_quantize_rows(int64_t rows, int32_t cols, const void *src, uint8_t *q
 
 /* Quantize-on-dispatch: token row x[t] (bf16, [T,d]) MX-quantized along d;
  * its qdata and scale rows are written to row dest_row[t,k] of qbuf
- * [R, d] and sbuf [R, d/32] for every route with dest_rank[t,k] ==
+ * [Rmax, d] and sbuf [Rmax, d/32] for every route with dest_rank[t,k] ==
  * ep_rank. Rows after the packed prefix are not written. T == 0: MOE_OK. */
 int moe_dispatch_rows_mx(const moe_shape_t *shape, const void *x, const int32_t *dest_rank,
                          const int32_t *dest_row, uint8_t *qbuf, uint8_t *sbuf,
@@ -323,10 +323,10 @@ int moe_dispatch_rows_mx(const moe_shape_t *shape, const void *x, const int32_t 
 /* MXFP8 grouped expert FFN over the packed prefix (offsets as moe_expert_ffn):
  * up:   H = silu(X W_gate^T) * (X W_up^T) from qbuf/sbuf and the quantized
  *       W_gu (w_gu_q [E_L,2F,d], w_gu_s [E_L,2F,d/32]); fp32 accumulation, H
- *       rounded to bf16 and MX-quantized along F into h_q [R, F] and
- *       h_s [R, F/32];
+ *       rounded to bf16 and MX-quantized along F into h_q [Rmax, F] and
+ *       h_s [Rmax, F/32];
  * down: Y = H W_d^T from h_q/h_s and the quantized W_d (w_d_q [E_L,d,F],
- *       w_d_s [E_L,d,F/32]); Y [R, d] bf16 (round to nearest even).
+ *       w_d_s [E_L,d,F/32]); Y [Rmax, d] bf16 (round to nearest even).
  * Only prefix rows are written. */
 int moe_expert_up_mx(const moe_shape_t *shape, const uint8_t *qbuf, const uint8_t *sbuf,
                      const int32_t *offsets, const uint8_t *w_gu_q, const uint8_t *w_gu_s,

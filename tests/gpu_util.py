@@ -136,8 +136,8 @@ def check_route(out: moe.RouteOut, ref: dict, shape: moe.MoeShape) -> None:
 
 
 def assert_row_src(got: np.ndarray, ref_rs: np.ndarray) -> None:
-    """row_src of R = moe_buffer_rows rows against the oracle's, which spans
-    the whole E_L*C capacity envelope: equal on the first R rows, and the
+    """row_src of Rmax = moe_buffer_rows rows against the oracle's, which spans
+    the whole E_L*C capacity envelope: equal on the first Rmax rows, and the
     oracle places no route past them (its rows there are -1)."""
     assert len(got) <= len(ref_rs)
     assert bool((ref_rs[len(got):] == -1).all()), "oracle route past the buffer rows"
