@@ -933,7 +933,7 @@ int launch_expert_ffn_bwd_data(const moe_shape_t &s, const void *buf, const int3
                                void *dgu, void *dx_rows, hipStream_t st) {
   const int E_L = s.N / s.ep_size;
   const int32_t *off = offsets + (size_t)s.ep_rank * (E_L + 1);
-  // 1. [G U] = X W_gu^T over the prefix rows (forward NT GEMM, no activation)
+  // [G U] = X W_gu^T over the prefix rows (forward NT GEMM, no activation)
   const int rc = launch_gemm_nt(s, buf, w_gu, off, gu, s.d, 2 * s.F, st);
   if (rc != MOE_OK) return rc;
   return launch_expert_ffn_bwd_data_gu(s, offsets, w_gu, w_down, dy, gu, dgu, dx_rows, st);
@@ -950,12 +950,12 @@ int launch_expert_ffn_bwd_data_gu(const moe_shape_t &s, const int32_t *offsets, 
   p.off = off;
   p.E_L = E_L;
   p.F = F;
-  // 2. dH = dY W_d (K = d, N = F), SwiGLU backward in the epilogue -> [dG dU]
+  // dH = dY W_d (K = d, N = F), SwiGLU backward on [G U] in the epilogue -> [dG dU]
   p.A = dy; p.lda = d; p.B = w_down; p.ldb = F; p.b_expert_stride = (int64_t)d * F;
   p.N = F; p.Kdim = d; p.gu = gu; p.Out = dgu; p.ldo = 2 * F;
   launch_mode<BW_DH>(s, p, st);
   if ((rc = launch_status()) != MOE_OK) return rc;
-  // 3. dX = [dG dU] W_gu (K = 2F, N = d)
+  // then dX = [dG dU] W_gu (K = 2F, N = d)
   p.A = dgu; p.lda = 2 * F; p.B = w_gu; p.ldb = d; p.b_expert_stride = (int64_t)2 * F * d;
   p.N = d; p.Kdim = 2 * F; p.gu = nullptr; p.Out = dx_rows; p.ldo = d;
   launch_mode<BW_DX>(s, p, st);
