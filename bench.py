@@ -392,7 +392,8 @@ def main():
         "data": "synthetic (seeded torch generator on the device; N(0,1) logits and x, "
                 "N(0,0.02^2) expert weights)",
         "config": {"workload": cfg.name, "T": T, "d": d, "N": N, "K": K, "F": F,
-                   "cf": str(cfg.cf), "capacity": cfg.capacity, "ep_size": cfg.ep_size,
+                   "cf": "dropless" if cfg.dropless else str(cfg.cf), "capacity": cfg.capacity,
+                   "buffer_rows": shape.rows, "ep_size": cfg.ep_size,
                    "ep_rank": cfg.ep_rank, "parallelism": "single GPU, all local experts"
                    if cfg.ep_size == 1 else f"one expert shard of {cfg.ep_size}"},
         "routed_rows": R, "source_tokens": S, "dropped_routes": drops,
