@@ -179,3 +179,34 @@ def test_layer_replays_from_a_captured_graph():
         torch.cuda.synchronize()
         assert torch.equal(layer.out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
         assert torch.equal(layer.route.dest_row, eager.route.dest_row)
+
+
+def test_largest_capacity_routes_like_capacity_t():
+    """Capacity 2^31 - 1 (the largest a shape holds): buffers of moe_buffer_rows
+    = T*min(K, E_L) rows, grids sized from them, every route kept; route map,
+    dispatch and layer output equal the oracle's with capacity T (no expert
+    can receive more than T routes, so the two capacities keep the same
+    routes)."""
+    base = LayerConfig("cap_max_bf16", T=700, d=128, N=12, K=3, F=128, cf=Fraction(1),
+                       dtype="bf16", ep_size=2, ep_rank=0, logits="zipf", seed=46)
+    print("[case] capacity 2^31-1", flush=True)
+    inp = make_inputs(base, "cpu")
+    shape = moe.MoeShape(T=base.T, d=base.d, N=base.N, K=base.K, F=base.F, ep_size=2,
+                         ep_rank=0, capacity=(1 << 31) - 1, dtype="bf16")
+    assert shape.rows == base.T * base.K
+    layer = moe.MoELayer(shape, "cuda")
+    for t in (layer.buf, layer.h, layer.y):
+        poison_(t)
+    layer.forward(inp.logits.cuda(), inp.x.cuda(), inp.w_gu.cuda(), inp.w_d.cuda())
+    torch.cuda.synchronize()
+    ref = orc.moe_layer(inp.logits.numpy(), inp.x.double().numpy(),
+                        inp.w_gu.double().numpy(), inp.w_d.double().numpy(), base.K, base.T,
+                        2, 0, "bf16")
+    assert int(ref["drop_mask"].sum()) == 0
+    assert_route_fields(layer.route, ref, ("counts", "offsets", "dest_rank", "dest_row",
+                                           "drop_mask", "row_src"))
+    n = int(ref["offsets"][0, -1])
+    np.testing.assert_array_equal(to_np(layer.buf[:n]), ref["buf"][:n])
+    assert bool(is_poison(layer.buf[n:]).all()) and bool(is_poison(layer.y[n:]).all())
+    assert_rows_close(to_np(layer.y[:n]), ref["y"][:n], tol_of("bf16"), "y")
+    assert_rows_close(to_np(layer.out), ref["out"], tol_of("bf16"), "out")
