@@ -2,12 +2,16 @@
 
 A step is one pass of the whole layer (route -> dispatch -> expert up (GEMM +
 SwiGLU) -> expert down -> combine) over one batch of seeded synthetic input
-already resident in HBM. Default workload: the OLMoE-shaped bf16 layer
-(T=8192, d=2048, 64 experts, top-8, F=1024, capacity factor 1.25).
+already resident in HBM. Default workload: the largest layer one GPU runs
+whole, the skewed-load bf16 layer (T=32768, d=4096, 128 experts, top-8,
+F=1536, capacity factor 1.25, Zipf(1.1)-biased router logits, so hot experts
+overflow and the drop path runs).
 
 Prints one JSON line. ``value`` is routed token-rows per second (kept routes
-to this GPU's experts per layer forward / layer time). Stage times come from
-HIP events recorded between the calls on the stream the kernels run on.
+to this GPU's experts per layer forward / mean layer time over the timed
+steps). Stage times come from HIP events recorded between the calls on the
+stream the kernels run on; the per-step median and spread are reported beside
+the mean.
 """
 from __future__ import annotations
 
@@ -30,9 +34,9 @@ STAGES = ["route", "dispatch", "up", "down", "combine"]
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="olmoe_bf16")
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="zipf_skew_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
@@ -255,6 +259,31 @@ def time_backward(args, layer, inp, stream, torch) -> dict:
                          "train_step_saving_ms": round(ms - ms_saved - (up_save_ms - up_ms), 5)}}
 
 
+def _quantile(sorted_vals, q):
+    """Linear-interpolation quantile of an ascending list."""
+    x = q * (len(sorted_vals) - 1)
+    i = int(x)
+    j = min(i + 1, len(sorted_vals) - 1)
+    return sorted_vals[i] + (sorted_vals[j] - sorted_vals[i]) * (x - i)
+
+
+def _range_push(name):
+    """Open a named range (roctx on ROCm) around the timed loop, so that a
+    rocprofv3 --hip-trace --marker-trace run can find the loop's API calls."""
+    try:
+        import torch
+        torch.cuda.nvtx.range_push(name)
+        return True
+    except Exception:   # no marker library: timing is unaffected
+        return False
+
+
+def _range_pop(opened):
+    if opened:
+        import torch
+        torch.cuda.nvtx.range_pop()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -304,10 +333,12 @@ def main():
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.set_sync_debug_mode("error")      # any host sync in the loop raises
+    marker = _range_push("steady_state_forward_loop")   # named range for a HIP API trace
     t_host0 = time.perf_counter()
     for s in range(args.steps):
         step(evs[s])
     t_host = time.perf_counter() - t_host0
+    _range_pop(marker)
     torch.cuda.set_sync_debug_mode(0)
     torch.cuda.synchronize()
 
@@ -331,6 +362,7 @@ def main():
 
     total_ms = evs[0][0].elapsed_time(evs[-1][5])
     ms_step = total_ms / args.steps
+    per_step = sorted(e[0].elapsed_time(e[5]) for e in evs)
     stage_ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
                 for i, name in enumerate(STAGES)}
 
@@ -385,6 +417,12 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_spread": {"median": round(_quantile(per_step, 0.5), 5),
+                               "min": round(per_step[0], 5),
+                               "p10": round(_quantile(per_step, 0.1), 5),
+                               "p90": round(_quantile(per_step, 0.9), 5),
+                               "max": round(per_step[-1], 5)},
+        "routed_rows_per_s_at_median": round(R / (_quantile(per_step, 0.5) * 1e-3), 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -456,6 +456,8 @@ class MoELayer:
         self.h = torch.empty(shape.rows, shape.F, dtype=dt, device=device)
         self.y = torch.empty(shape.rows, shape.d, dtype=dt, device=device)
         self.out = torch.empty(shape.T, shape.d, dtype=dt, device=device)
+        # which forward filled the buffers last: "bf16", "mx" or None
+        self.last_forward = None
 
     def route_step(self, logits, stream=None):
         moe_route(self.shape, logits, self.route, self.ws, stream)
@@ -490,6 +492,7 @@ class MoELayer:
         self.up_step(w_gu, stream, save_gu)
         self.down_step(w_d, stream)
         self.combine_step(stream)
+        self.last_forward = "bf16"
         return self.out
 
     def alloc_mx(self, device="cuda") -> None:
@@ -515,8 +518,9 @@ class MoELayer:
                            mxw.w_d_s, self.y, stream)
 
     def forward_mx(self, logits, x, mxw: "MxWeights", stream=None) -> torch.Tensor:
-        """MXFP8 forward: the same routing, quantize-on-dispatch, MXFP8 expert
-        GEMMs on the quantized weights, BF16 combine."""
+        """MXFP8 forward (inference only: ``backward`` refuses to follow it):
+        the same routing, quantize-on-dispatch, MXFP8 expert GEMMs on the
+        quantized weights, BF16 combine."""
         if not hasattr(self, "qbuf"):
             self.alloc_mx(self.out.device)
         self.gu_saved = False
@@ -525,6 +529,7 @@ class MoELayer:
         self.up_mx_step(mxw, stream)
         self.down_mx_step(mxw, stream)
         self.combine_step(stream)
+        self.last_forward = "mx"
         return self.out
 
     def alloc_backward(self, device="cuda") -> None:
@@ -544,7 +549,14 @@ class MoELayer:
     def backward(self, dout, w_gu, w_d, stream=None):
         """Gradients of the last forward for the output gradient ``dout``:
         returns (dx, dlogits, dw_gu, dw_down), enqueued on the stream with no
-        host synchronization."""
+        host synchronization. The last forward must be the BF16 ``forward``:
+        the MXFP8 forward keeps no BF16 dispatch rows or H, so a backward after
+        it (or before any forward) raises instead of differentiating stale
+        buffers."""
+        if self.last_forward != "bf16":
+            raise RuntimeError(
+                "MoELayer.backward needs the BF16 forward as the last forward "
+                f"(last forward: {self.last_forward!r}; the MXFP8 forward is inference-only)")
         if not hasattr(self, "dy"):
             self.alloc_backward(self.out.device)
         s, r = self.shape, self.route

@@ -14,6 +14,7 @@ MOE_EWORKSPACE = -4
 MOE_EHIP = -5
 MOE_MAX_K = 16
 MOE_MAX_EXPERTS = 1024
+MOE_MAX_WIDTH = 1 << 20
 MOE_F32 = 0
 MOE_BF16 = 1
 

@@ -394,7 +394,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bwd(GemmArgs p) {
 
 // ---- bf16 big tiles: the forward's pipeline for operands of any layout.
 // 256 x 256 block tile, K step 64, two LDS stages, 8 waves of 128 x 64 (4 x 2
-// MFMA 32x32x16 tiles each; 4 waves of 128 x 128 with MOE_BWD_WAVES = 4),
+// MFMA 32x32x16 tiles each),
 // operands loaded global -> LDS directly and the
 // loads of step k+1 issued between the MFMAs of step k (as in the forward).
 // Two LDS tile layouts per stage (32 KiB per operand):
@@ -413,11 +413,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bwd(GemmArgs p) {
 // the B rows past the range in LDS before its MFMAs.
 // Waves per block: 8 (128 x 64 wave tiles) measured 3-4% faster here than 4
 // (128 x 128), the reverse of the forward kernel.
-#ifndef MOE_BWD_WAVES
-#define MOE_BWD_WAVES 8
-#endif
 namespace bt {
-constexpr int BM = 256, BN = 256, BK = 64, NW = MOE_BWD_WAVES, NT = 64 * NW;
+constexpr int BM = 256, BN = 256, BK = 64, NW = 8, NT = 64 * NW;
 constexpr int WAVES_N = NW / 2;        // 2 wave rows of 128 x WAVES_N wave columns
 constexpr int WTN = BN / WAVES_N;      // output columns per wave
 constexpr int TM = 4, TN = WTN / 32;   // 32 x 32 MFMA tiles per wave
@@ -558,7 +555,10 @@ __global__ __launch_bounds__(bt::NT, 1) void k_gemm_bwd_big(GemmArgs p) {
   const int khalf = lane >> 5, fr = lane & 31;
 
   BigCtx c;
-  c.A = static_cast<const uint16_t *>(p.A);
+  // K-contiguous A rows are addressed from the tile's first row (64-bit
+  // base), so the 32-bit offsets stay below BM * lda wherever the tile lies
+  c.A = static_cast<const uint16_t *>(p.A) +
+        (MODE == BW_WG ? (size_t)0 : (size_t)wk.m0 * p.lda);
   c.Bj = static_cast<const uint16_t *>(p.B) +
          (MODE == BW_WG ? 0 : (int64_t)wk.expert * p.b_expert_stride);
   c.lda = p.lda;
@@ -582,8 +582,8 @@ __global__ __launch_bounds__(bt::NT, 1) void k_gemm_bwd_big(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < bt::LPW; ++i) {
       const int r = (wv * bt::LPW + i) * 8 + lrow;
-      const int grow = min(wk.m0 + r, wk.m_end - 1);   // clamped rows are discarded
-      c.a_off[i] = (uint32_t)grow * (uint32_t)p.lda + ((kch ^ chunk_swz<8>(r)) << 3);
+      const int tr = min(r, wk.m_end - 1 - wk.m0);   // clamped rows are discarded
+      c.a_off[i] = (uint32_t)tr * (uint32_t)p.lda + ((kch ^ chunk_swz<8>(r)) << 3);
     }
   }
   {

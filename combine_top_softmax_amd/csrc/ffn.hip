@@ -51,11 +51,12 @@ struct Tile {
 };
 
 // Map this block to a (expert, m-tile, n-tile) from the local offsets (the
-// shared lookup above; wave-uniform). Inside an expert with M m-tiles, tiles
-// go in groups of NG n-tiles: all M m-tiles of the first NG n-tiles, then the
-// next group, so the tiles that run at the same time on one XCD share both
-// their A rows and their weight panels in L2.
-template <int NG>
+// shared lookup above; wave-uniform). Inside an expert with M m-tiles, the
+// tiles of one weight panel come first: all M m-tiles of n-tile 0, then of
+// n-tile 1, ..., so the tiles that run at the same time on one XCD share their
+// weight panel and the expert's A rows in L2 (equal or best on every named
+// workload among groups of 1, 2, 4 and 8 n-tiles and "all n-tiles of an
+// m-tile first").
 __device__ __forceinline__ Tile find_tile(const int32_t *__restrict__ off, int E_L, int bm,
                                           int n_tiles_n) {
   Tile tl;
@@ -63,34 +64,14 @@ __device__ __forceinline__ Tile find_tile(const int32_t *__restrict__ off, int E
   tl.valid = x.valid;
   if (!x.valid) return tl;
   const int li = x.L - x.mstart * n_tiles_n;   // tile index inside the expert, < M * n_tiles_n
-  const int g = li / (x.M * NG);               // n-group
-  const int w = min(NG, n_tiles_n - g * NG);   // n-tiles in this group
-  const int r = li - g * NG * x.M;
+  const int n = li / x.M;                      // n-tile
   tl.expert = x.e;
-  tl.row0 = x.row_begin + (r / w) * bm;
+  tl.row0 = x.row_begin + (li - n * x.M) * bm;
   tl.row_end = x.row_end;
-  tl.n_idx = g * NG + r % w;
+  tl.n_idx = n;
   return tl;
 }
 
-// n-tiles per group in the tile order (1 = all m-tiles of one n-tile, then the
-// next n-tile): equal or best on every named workload among 1, 2, 4, 8 and
-// "all n-tiles of an m-tile first".
-// Waves per big-tile block: 4 (one per SIMD, 128 x 128 wave tiles, 256
-// accumulators each) measured 2-5% faster than 8 (two per SIMD, 128 x 64
-// wave tiles) on the named workloads once the fragment-read waits were exact:
-// square wave tiles read a third fewer bytes from LDS per flop, and this
-// kernel runs power-limited (the shader clock drops to ~1.3-1.6 GHz in its
-// main loop), so less data movement buys clock.
-#ifndef MOE_GEMM_WAVES
-#define MOE_GEMM_WAVES 4
-#endif
-#ifndef MOE_BSTAGES
-#define MOE_BSTAGES 3
-#endif
-#ifndef MOE_TILE_NGROUP
-#define MOE_TILE_NGROUP 1
-#endif
 
 // ------------------------------------------------------------------ bf16 MFMA
 constexpr int kBM = 128;        // rows per block tile
@@ -112,7 +93,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kLds];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBW * kLds];
 
-  const Tile tl = find_tile<MOE_TILE_NGROUP>(off, E_L, kBM, n_tiles_n);
+  const Tile tl = find_tile(off, E_L, kBM, n_tiles_n);
   if (!tl.valid) return;
 
   const int tid = threadIdx.x;
@@ -223,17 +204,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(
 }
 
 // ------------------------------------------------------------ bf16 MFMA, big tiles
-// Block tile BM rows x 256 weight rows, K step BK, two LDS stages for the A
-// rows and NS (2 or 3) for the weight rows, NW waves (the library
-// instantiates BM = 256, BK = 64, NS = 3, NW = 4; the template also covers
-// BM = 128, BK = 32 and NW = 8, which measured slower):
-//   NW = 8, BM = 256: 2 x 4 waves of 128 x 64 (4 x 2 MFMA tiles, 128 accumulators)
-//   NW = 4, BM = 256: 2 x 2 waves of 128 x 128 (4 x 4 MFMA tiles, 256 accumulators)
+// Block tile 256 rows x 256 weight rows, K step 64, two LDS stages for the A
+// rows and three for the weight rows, 4 waves: 2 x 2 waves of 128 x 128 (4 x
+// 4 MFMA tiles, 256 accumulators each, one wave per SIMD). Square wave tiles
+// read a third fewer LDS bytes per flop than 8 waves of 128 x 64, and the
+// kernel runs power-limited (the shader clock drops to ~1.3-1.6 GHz in its
+// main loop), so the 4-wave layout measured 2-5% faster on every named
+// workload; 128-row tiles and 32-wide K steps measured slower.
 // Operands go global -> LDS directly (global_load_lds_dwordx4, no VGPR
 // staging). Step k, right after its opening barrier, issues the A loads of
-// step k + 1 and then the weight loads of step k + NS - 1: the weight rows
+// step k + 1 and then the weight loads of step k + 2: the weight rows
 // (each read from HBM once per expert, shared by fewer tiles than the A rows)
-// get NS - 1 steps of MFMA work to land, the A rows one (2 x 32 KiB + 3 x 32
+// get two steps of MFMA work to land, the A rows one (2 x 32 KiB + 3 x 32
 // KiB fill the 160 KiB of LDS). The barrier is a plain s_barrier preceded by
 // a wait for this wave's loads of the step about to be read (s_waitcnt
 // vmcnt(N) with N = the younger weight loads still allowed in flight), not a
@@ -242,9 +224,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(
 // c ^ swz(r), chosen so that a wave's direct load writes whole rows
 // contiguously and the fragment reads of 16 consecutive rows (one chunk each)
 // touch 16 distinct 16-byte bank groups. Requires K % BK == 0.
-template <int BM, int BK, int NS, int NW = 4>
 struct BigTile {
-  static constexpr int NWAVES = NW;              // waves per block
+  static constexpr int BM = 256;                 // rows per block
+  static constexpr int BK = 64;                  // K per main-loop step
+  static constexpr int NS = 3;                   // LDS stages of the weight rows
+  static constexpr int NW = 4;                   // waves per block
   static constexpr int BW = 256;                 // weight rows per block
   static constexpr int WAVES_M = BM / 128;
   static constexpr int WAVES_N = NW / WAVES_M;
@@ -260,17 +244,15 @@ struct BigTile {
   static constexpr int KS = BK / 16;             // MFMA K sub-steps per step
   static constexpr int A_BYTES = BM * ROW_B;     // one A stage
   static constexpr int B_BYTES = BW * ROW_B;     // one B stage
-  static constexpr int STAGE_BYTES = (BM + BW) * ROW_B;
 };
 
 
 // Issue the direct global -> LDS loads of one K step into `stage`.
-template <int BM, int BK, int NS, int NW>
 __device__ __forceinline__ void big_issue(const uint16_t *__restrict__ A,
                                           const uint16_t *__restrict__ Wj, const uint32_t *a_off,
                                           const uint32_t *b_off, int ka, int kb, int wv,
                                           uint32_t sa, uint32_t sb, bool do_a) {
-  using P = BigTile<BM, BK, NS, NW>;
+  using P = BigTile;
   if (do_a) {
 #pragma unroll
     for (int i = 0; i < P::NA; ++i) dma16(A + a_off[i] + ka, sa + (wv * P::NA + i) * 1024);
@@ -299,22 +281,21 @@ __device__ __forceinline__ void big_issue(const uint16_t *__restrict__ A,
 // dropped at compile time, and the A direct loads in a_skip (bit d: load d
 // feeds only rows past the last valid 32-row group) are not issued. Full
 // tiles take VT = TM.
-template <bool GATE_UP, int BM, int BK, int NS, int NW, int VT = BigTile<BM, BK, NS, NW>::TM>
+template <bool GATE_UP, int VT = BigTile::TM>
 __device__ __forceinline__ void big_step(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ Wj, const uint32_t *a_off,
     const uint32_t *b_off, int ka, int kb, int wv, uint32_t lda, uint32_t ldb,
     const uint8_t *__restrict__ rda, const uint8_t *__restrict__ rdb, const int *fa,
     const int *fb, int khalf, int sw,
-    f32x16_t (&acc)[BigTile<BM, BK, NS, NW>::TM][BigTile<BM, BK, NS, NW>::TN],
-    bf16x8_t (&fra)[2][BigTile<BM, BK, NS, NW>::TM], bf16x8_t (&frb)[2][BigTile<BM, BK, NS, NW>::TN],
+    f32x16_t (&acc)[BigTile::TM][BigTile::TN], bf16x8_t (&fra)[2][BigTile::TM],
+    bf16x8_t (&frb)[2][BigTile::TN],
     uint32_t a_skip = 0) {
-  using P = BigTile<BM, BK, NS, NW>;
+  using P = BigTile;
   constexpr bool PARTIAL = VT < P::TM;
   constexpr int MF = P::KS * P::TM * P::TN;      // MFMAs per step
   constexpr int MS = P::TM * P::TN;              // MFMAs per sub-step
-  // MFMAs between two direct loads: spread over the step, or over its first
-  // half with two stages (those loads must land before the next step)
-  constexpr int GAP = (NS == 2 && MF >= 2 * P::L) ? MF / (2 * P::L) : MF / P::L;
+  // MFMAs between two direct loads: spread over the whole step
+  constexpr int GAP = MF / P::L;
   static_assert(GAP >= 1 && GAP * P::L <= MF, "load spacing");
   constexpr FragOrder<P::TM, P::TN> ord{};
   auto issue_one = [&](int d) {
@@ -358,12 +339,13 @@ __device__ __forceinline__ void big_step(
 
 // Epilogue of the big-tile kernels (every wave past its last MFMA, every
 // direct load drained, the stages free).
-template <bool GATE_UP, bool SAVE, int BM, int NW>
+template <bool GATE_UP, bool SAVE>
 __device__ __forceinline__ void big_epilogue(
-    const f32x16_t (&acc)[BigTile<BM, 64, 2, NW>::TM][BigTile<BM, 64, 2, NW>::TN],
+    const f32x16_t (&acc)[BigTile::TM][BigTile::TN],
     uint8_t *__restrict__ smem, const Tile &tl, uint16_t *__restrict__ Out,
     uint16_t *__restrict__ GU, int Nout, int n0, int wm, int wn) {
-  using P = BigTile<BM, 64, 2, NW>;
+  using P = BigTile;
+  constexpr int BM = P::BM, NW = P::NW;
   static_assert(!SAVE || GATE_UP, "only the gate/up product has a [G U] tile to keep");
   // Epilogue, staged through LDS so that global stores are whole 16-byte
   // vectors along output rows. The MFMAs take the weight fragment as their
@@ -505,20 +487,20 @@ __device__ __forceinline__ void big_epilogue(
 
 // SAVE (gate/up product only): also keep the pre-activation [G U] rows in GU
 // ([rows, 2 Nout], gate columns then up columns) for the backward.
-template <bool GATE_UP, bool SAVE, int BM, int BK, int NS, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
+template <bool GATE_UP, bool SAVE>
+__global__ __launch_bounds__(64 * BigTile::NW, 1) void k_gemm_bf16_big(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
     const int32_t *__restrict__ off, uint16_t *__restrict__ Out, uint16_t *__restrict__ GU,
     int E_L, int Kdim, int Nout, int n_tiles_n) {
-  using P = BigTile<BM, BK, NS, NW>;
-  // two A stages, NS B stages (NS = 3: the weight rows, which miss to HBM
-  // more often, get two steps to land)
-  static_assert(NS == 2 || NS == 3, "B stages");
+  using P = BigTile;
+  constexpr int BM = P::BM, BK = P::BK, NS = P::NS;
+  // two A stages, NS = 3 B stages: the weight rows, which miss to HBM more
+  // often, get two steps to land
   constexpr int B_BASE = 2 * P::A_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[B_BASE + NS * P::B_BYTES];
 
   const uint32_t smem_l = lds_addr(smem);
-  const Tile tl = find_tile<MOE_TILE_NGROUP>(off, E_L, BM, n_tiles_n);
+  const Tile tl = find_tile(off, E_L, BM, n_tiles_n);
   if (!tl.valid) return;
 
   const int tid = threadIdx.x;
@@ -530,15 +512,19 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
   const int n0 = tl.n_idx * (GATE_UP ? P::BW / 2 : P::BW);
 
   // direct-load sources (element offsets): lane -> row RPI*instr + lane/CH,
-  // physical chunk lane%CH
+  // physical chunk lane%CH. The A rows are addressed from the tile's first
+  // row At (64-bit), so an offset stays below BM * Kdim however far into the
+  // buffer the tile lies; weight rows stay below 2F * d < 2^31 elements of
+  // the expert's matrix (checked on the host).
+  const uint16_t *At = A + (size_t)tl.row0 * Kdim;
   uint32_t a_off[P::NA], b_off[P::NB];
   {
     const int lrow = lane / P::CH, pch = lane % P::CH;
 #pragma unroll
     for (int i = 0; i < P::NA; ++i) {
       const int r = (wv * P::NA + i) * P::RPI + lrow;
-      const int grow = min(tl.row0 + r, tl.row_end - 1);   // clamped rows are discarded
-      a_off[i] = (uint32_t)grow * (uint32_t)Kdim + ((pch ^ chunk_swz<P::CH>(r)) << 3);
+      const int tr = min(r, tl.row_end - 1 - tl.row0);   // clamped rows are discarded
+      a_off[i] = (uint32_t)tr * (uint32_t)Kdim + ((pch ^ chunk_swz<P::CH>(r)) << 3);
     }
 #pragma unroll
     for (int i = 0; i < P::NB; ++i) {
@@ -591,7 +577,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
   // rely on every A load of a step being issued before that step's B loads)
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    big_issue<BM, BK, NS, NW>(A, Wj, a_off, b_off, 0, min(s, nk - 1) * BK, wv, smem_l,
+    big_issue(At, Wj, a_off, b_off, 0, min(s, nk - 1) * BK, wv, smem_l,
                               smem_l + B_BASE + s * P::B_BYTES, s == 0);
   // one main loop per count of valid 32-row tiles of this wave (TM for full
   // tiles; fewer on an expert's last m-tile), each with a single inlined step
@@ -613,9 +599,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
       const uint32_t ldb = smem_l + B_BASE + ((kb + NS - 1) % NS) * P::B_BYTES;
       const uint8_t *rda = smem + (kb & 1) * P::A_BYTES;
       const uint8_t *rdb = smem + B_BASE + (kb % NS) * P::B_BYTES;
-      big_step<GATE_UP, BM, BK, NS, NW, VT>(A, Wj, a_off, b_off, min(kb + 1, nk - 1) * BK,
-                                            min(kb + NS - 1, nk - 1) * BK, wv, lda, ldb, rda,
-                                            rdb, fa, fb, khalf, sw, acc, fra, frb, a_skip);
+      big_step<GATE_UP, VT>(At, Wj, a_off, b_off, min(kb + 1, nk - 1) * BK,
+                            min(kb + NS - 1, nk - 1) * BK, wv, lda, ldb, rda, rdb, fa, fb, khalf,
+                            sw, acc, fra, frb, a_skip);
     }
   };
   static_assert(P::TM == 4, "main-loop variants");
@@ -629,7 +615,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16_big(
 
   wait_vmcnt<0>();   // no direct load still in flight into the stages
   __syncthreads();   // every wave is done reading the last stage
-  big_epilogue<GATE_UP, SAVE, BM, NW>(acc, smem, tl, Out, GU, Nout, n0, wm, wn);
+  big_epilogue<GATE_UP, SAVE>(acc, smem, tl, Out, GU, Nout, n0, wm, wn);
 }
 
 // ------------------------------------------------------------------ fp32 SIMT
@@ -641,7 +627,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(
     float *__restrict__ Out, int E_L, int Kdim, int Nout, int n_tiles_n) {
   __shared__ float sA[kFK][kFM + 1];
   __shared__ float sB[kFK][kFW + 1];
-  const Tile tl = find_tile<MOE_TILE_NGROUP>(off, E_L, kFM, n_tiles_n);
+  const Tile tl = find_tile(off, E_L, kFM, n_tiles_n);
   if (!tl.valid) return;
   const int tid = threadIdx.x;
   const int ty = tid >> 4, tx = tid & 15;
@@ -711,25 +697,23 @@ inline unsigned grid_blocks(const moe_shape_t &s, int bm, int n_tiles_n) {
   return (unsigned)(ceil_div(max_m * n_tiles_n, kNumXcd) * kNumXcd);
 }
 
-// Which bf16 kernel runs: the big-tile kernel (BM = 256, BK = 64, two
-// stages: the fastest of the tile / K-step / stage-count variants measured
-// on the named workloads) when K % 64 == 0, else the 128 x 128
-// register-staged kernel (any K % 8 == 0).
+// Which bf16 kernel runs: the big-tile kernel (256 x 256 tiles, K step 64)
+// when K % 64 == 0, else the 128 x 128 register-staged kernel (any
+// K % 8 == 0).
 template <bool GATE_UP>
 int launch_bf16(const moe_shape_t &s, const uint16_t *A, const uint16_t *W, const int32_t *off,
                 uint16_t *Out, int Kdim, int Nout, hipStream_t st, uint16_t *GU = nullptr) {
   const int E_L = s.N / s.ep_size;
   if (Kdim % 64 == 0) {
-    constexpr int BM = 256;
-    const int ntn = (int)ceil_div(Nout, GATE_UP ? 128 : 256);
+    using P = BigTile;
+    const int ntn = (int)ceil_div(Nout, GATE_UP ? P::BW / 2 : P::BW);
+    const dim3 grid(grid_blocks(s, P::BM, ntn)), block(64 * P::NW);
     if (GATE_UP && GU != nullptr)
-      hipLaunchKernelGGL((k_gemm_bf16_big<true, true, BM, 64, MOE_BSTAGES, MOE_GEMM_WAVES>),
-                         dim3(grid_blocks(s, BM, ntn)), dim3(64 * MOE_GEMM_WAVES), 0, st, A, W,
-                         off, Out, GU, E_L, Kdim, Nout, ntn);
+      hipLaunchKernelGGL((k_gemm_bf16_big<true, true>), grid, block, 0, st, A, W, off, Out, GU,
+                         E_L, Kdim, Nout, ntn);
     else
-      hipLaunchKernelGGL((k_gemm_bf16_big<GATE_UP, false, BM, 64, MOE_BSTAGES, MOE_GEMM_WAVES>),
-                         dim3(grid_blocks(s, BM, ntn)), dim3(64 * MOE_GEMM_WAVES), 0, st, A, W,
-                         off, Out, nullptr, E_L, Kdim, Nout, ntn);
+      hipLaunchKernelGGL((k_gemm_bf16_big<GATE_UP, false>), grid, block, 0, st, A, W, off, Out,
+                         nullptr, E_L, Kdim, Nout, ntn);
   } else {
     const int ntn = (int)ceil_div(Nout, GATE_UP ? kBW / 2 : kBW);
     hipLaunchKernelGGL(k_gemm_bf16<GATE_UP>, dim3(grid_blocks(s, kBM, ntn)), dim3(256), 0, st,

@@ -14,8 +14,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // touch 16 distinct 16-byte bank groups.
 template <int CH>
 __device__ __forceinline__ int chunk_swz(int r) {
-  if constexpr (CH == 8) return (r & 7) ^ ((r >> 3) & 1);
-  else return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
+  static_assert(CH == 8, "rows of 8 chunks (64 bf16 or 128 fp8 elements)");
+  return (r & 7) ^ ((r >> 3) & 1);
 }
 
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))

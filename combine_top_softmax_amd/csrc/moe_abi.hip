@@ -10,6 +10,8 @@ namespace {
 
 using moe::ceil_div;
 
+constexpr int64_t kLim31 = (int64_t)1 << 31;
+
 bool aligned16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool aligned4(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
 
@@ -24,7 +26,18 @@ int check_shape(const moe_shape_t *s) {
   if (s->d % 8 != 0 || s->F % 8 != 0) return MOE_EINVAL;
   // the buffer rows, the offsets and every row index stay below T*K (or
   // min(K, E_L) for an empty batch), whatever the capacity
-  if ((int64_t)s->T * s->K >= (int64_t)1 << 31) return MOE_EINVAL;
+  if ((int64_t)s->T * s->K >= kLim31) return MOE_EINVAL;
+  // 32-bit offsets inside the GEMMs: a tile's A rows are addressed from its
+  // first row (at most 256 rows of d or 2F elements past a 64-bit base), and
+  // a weight row inside one expert's matrix (fewer than 2F*d elements)
+  if (s->d > MOE_MAX_WIDTH || s->F > MOE_MAX_WIDTH) return MOE_EINVAL;
+  if ((int64_t)2 * s->F * s->d >= kLim31) return MOE_EINVAL;
+  // tile counts of the grouped GEMMs (the smallest tiles: 64 rows, 32 output
+  // columns) fit a signed 32-bit grid index
+  const int64_t E_L = s->N / s->ep_size;
+  const int64_t m_tiles = moe::ceil_div(moe::buffer_rows(*s), 64) + E_L;
+  const int64_t n_tiles = moe::ceil_div(2 * (int64_t)s->F > s->d ? 2 * (int64_t)s->F : s->d, 32);
+  if (m_tiles * n_tiles >= kLim31) return MOE_EINVAL;
   return MOE_OK;
 }
 

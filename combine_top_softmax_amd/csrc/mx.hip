@@ -131,15 +131,12 @@ __global__ __launch_bounds__(256) void k_quant_rows(
 }
 
 // ------------------------------------------------------------ MX grouped GEMM
-// Waves per MX block: 8 (two per SIMD, 128 x 64 wave tiles) or 4 (one per
-// SIMD, 128 x 128 wave tiles, a third fewer LDS fragment bytes per flop). 8
-// measured 1-5% faster than 4 on the named workloads: with two LDS stages
-// and a full wait per step, a second wave per SIMD covers more of the stalls.
-#ifndef MOE_MX_WAVES
-#define MOE_MX_WAVES 8
-#endif
+// Waves per MX block: 8 (two per SIMD, 128 x 64 wave tiles). 4 waves (one per
+// SIMD, 128 x 128 wave tiles, a third fewer LDS fragment bytes per flop)
+// measured 1-5% slower on the named workloads: with two LDS stages and a full
+// wait per step, a second wave per SIMD covers more of the stalls.
 namespace mxg {
-constexpr int BM = 256, BW = 256, BK = 128, NW = MOE_MX_WAVES, NT = 64 * NW;
+constexpr int BM = 256, BW = 256, BK = 128, NW = 8, NT = 64 * NW;
 constexpr int WAVES_N = NW / 2, WTN = BW / WAVES_N;   // weight rows per wave
 constexpr int TM = 4, TN = WTN / 32;             // 4 x TN MFMA tiles per wave
 constexpr int SPW = 8 / NW;                      // scale-dword loads per wave and step
@@ -292,7 +289,9 @@ __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
   const int kb32 = Kdim >> 5;               // scale bytes per row
 
   MxCtx c;
-  c.A = A;
+  // A rows and their scale rows are addressed from the tile's first row
+  // (64-bit bases), so the 32-bit offsets stay below BM * Kdim
+  c.A = A + (size_t)tl.row0 * Kdim;
   c.W = W + (size_t)tl.expert * Nw * Kdim;
   auto wrow_of = [&](int r) {               // block weight row r -> weight row
     if (GATE_UP)
@@ -304,8 +303,8 @@ __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
 #pragma unroll
     for (int i = 0; i < mxg::NA; ++i) {
       const int r = (wv * mxg::NA + i) * mxg::RPI + lrow;
-      const int grow = min(tl.row0 + r, tl.row_end - 1);   // clamped rows are discarded
-      c.a_off[i] = (uint32_t)grow * (uint32_t)Kdim + ((pch ^ chunk_swz<8>(r)) << 4);
+      const int tr = min(r, tl.row_end - 1 - tl.row0);   // clamped rows are discarded
+      c.a_off[i] = (uint32_t)tr * (uint32_t)Kdim + ((pch ^ chunk_swz<8>(r)) << 4);
     }
 #pragma unroll
     for (int i = 0; i < mxg::NB; ++i) {
@@ -322,8 +321,8 @@ __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
     const int u = wv * mxg::SPW + j;
     const int r = (u & 3) * 64 + lane;
     if (u < 4) {
-      c.S[j] = As;
-      c.s_off[j] = (uint32_t)min(tl.row0 + r, tl.row_end - 1) * (uint32_t)kb32;
+      c.S[j] = As + (size_t)tl.row0 * kb32;
+      c.s_off[j] = (uint32_t)min(r, tl.row_end - 1 - tl.row0) * (uint32_t)kb32;
       c.s_dst[j] = mxg::SC_OFF + (u & 3) * 256;
     } else {
       c.S[j] = Ws + (size_t)tl.expert * Nw * kb32;

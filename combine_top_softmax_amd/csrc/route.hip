@@ -383,7 +383,8 @@ __global__ __launch_bounds__(64) void k_assign(
   }
   if (row_src != nullptr) {
     const int used = s_g[(ep_rank + 1) * E_L] - s_g[ep_rank * E_L];
-    for (int r = used + tile * kWave + lane; r < rows; r += ntiles * kWave) row_src[r] = -1;
+    for (int64_t r = used + (int64_t)tile * kWave + lane; r < rows; r += (int64_t)ntiles * kWave)
+      row_src[r] = -1;
   }
 }
 

@@ -58,6 +58,7 @@ typedef struct ihipStream_t *hipStream_t;
 /* Limits of this implementation (MOE_EINVAL beyond them). */
 #define MOE_MAX_K        16     /* top-K                     */
 #define MOE_MAX_EXPERTS  1024   /* N                         */
+#define MOE_MAX_WIDTH    (1 << 20)  /* d and F                */
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
@@ -66,7 +67,10 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
  * capacity C, and the dtype of x / buf / weights / h / y / out.
  * Validated: T >= 0 and every other size >= 1, K <= N, K <= MOE_MAX_K,
  * N <= MOE_MAX_EXPERTS, N % ep_size == 0, 0 <= ep_rank < ep_size, d and F
- * multiples of 8, T*K < 2^31. Any capacity C >= 1 is valid; C >= T keeps
+ * multiples of 8 and at most MOE_MAX_WIDTH, T*K < 2^31, 2*F*d < 2^31 (one
+ * expert's weight matrix; the GEMMs address a weight row and a tile's rows
+ * with 32-bit offsets from 64-bit bases), and the grouped-GEMM tile count
+ * (ceil(Rmax/64) + E_L) * ceil(max(2F, d)/32) < 2^31. Any capacity C >= 1 is valid; C >= T keeps
  * every route (no expert can receive more than T routes): the dropless mode,
  * with buffers of the upper-bound size Rmax below and no host-visible count.
  * An empty batch (T == 0) is valid: moe_route / moe_route_map write zero

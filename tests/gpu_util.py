@@ -44,21 +44,59 @@ def tol_of(dtype: str) -> float:
     return 2e-2 if dtype == "bf16" else 1e-4
 
 
+# Every floating-point comparison made through the helpers below, for the
+# end-of-session report (conftest.py prints it; PARITY_REPORT=<path> also
+# writes it as JSON): test, quantity, rows compared, worst per-row relative L2
+# error, worst element error relative to its scale (max(|ref|, row rms), or
+# the Cauchy-Schwarz bound of assert_bounded; either is held to the
+# tolerance), largest absolute difference.
+REPORT: list = []
+
+
+def _record(what: str, rows: int, worst_row: float, worst_elem: float, max_abs: float,
+            tol: float) -> None:
+    import os
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    REPORT.append(dict(test=test, what=what, rows=int(rows), tol=tol, worst_row_l2=worst_row,
+                       worst_elem_rel=worst_elem, max_abs_err=max_abs))
+
+
 def assert_rows_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str) -> float:
-    """Per-row relative L2 error <= tol; rows that are exactly zero in the
-    reference must be exactly zero. Returns the worst per-row error."""
+    """Element by element and row by row: for every element
+    |got - ref| <= tol * max(|ref|, rms(ref row)), and for every row the
+    relative L2 error ||got - ref|| / ||ref|| <= tol; rows that are exactly
+    zero in the reference must be exactly zero. The element bound is relative
+    to the element itself, floored at the row's rms so that elements near
+    zero (where a 1-ulp storage rounding is a large relative change) are held
+    to the row's scale. Records the worst values (see REPORT) and returns the
+    worst per-row error."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    if got.ndim == 1:
+        got, ref = got[None], ref[None]
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     zero = np.all(ref == 0, axis=1)
     assert np.all(got[zero] == 0), f"{what}: rows that must be exactly zero are not"
     nz = ~zero
     if not np.any(nz):
+        _record(what, len(ref), 0.0, 0.0, 0.0, tol)
         return 0.0
-    err = np.linalg.norm(got[nz] - ref[nz], axis=1) / np.linalg.norm(ref[nz], axis=1)
-    worst = float(err.max())
+    g, r = got[nz], ref[nz]
+    diff = np.abs(g - r)
+    norm = np.linalg.norm(r, axis=1)
+    err = np.linalg.norm(g - r, axis=1) / norm
+    rms = norm / np.sqrt(r.shape[1])
+    bound = np.maximum(np.abs(r), rms[:, None])
+    elem = diff / bound
+    worst, worst_e, max_abs = float(err.max()), float(elem.max()), float(diff.max())
+    _record(what, len(ref), worst, worst_e, max_abs, tol)
     assert worst <= tol, f"{what}: worst per-row relative L2 error {worst:.3e} > {tol:.1e}"
+    if worst_e > tol:
+        i, j = np.unravel_index(int(np.argmax(elem)), elem.shape)
+        raise AssertionError(
+            f"{what}: element ({i}, {j}) of the nonzero rows off by {diff[i, j]:.3e} = "
+            f"{worst_e:.3e} x max(|ref|, row rms) > {tol:.1e} (got {g[i, j]!r}, ref {r[i, j]!r})")
     return worst
 
 
@@ -77,9 +115,12 @@ def assert_bounded(got: np.ndarray, ref: np.ndarray, scale: np.ndarray, tol: flo
     zero = scale == 0
     assert np.all(got[zero] == ref[zero]), f"{what}: entries with a zero bound differ"
     if not np.any(~zero):
+        _record(what, got.shape[0], 0.0, 0.0, 0.0, tol)
         return 0.0
-    r = np.abs(got[~zero] - ref[~zero]) / scale[~zero]
+    diff = np.abs(got[~zero] - ref[~zero])
+    r = diff / scale[~zero]
     worst = float(r.max())
+    _record(what, got.shape[0], float("nan"), worst, float(diff.max()), tol)
     assert worst <= tol, f"{what}: worst error / bound {worst:.3e} > {tol:.1e}"
     return worst
 

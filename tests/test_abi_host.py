@@ -48,6 +48,13 @@ BASE = dict(T=64, d=64, N=8, K=2, F=64, ep_size=2, ep_rank=1, capacity=16, dtype
     (dict(N=2048, K=2, ep_size=1, ep_rank=0), _abi.MOE_EINVAL),
     (dict(N=32, K=17, ep_size=1, ep_rank=0), _abi.MOE_EINVAL),
     (dict(T=1 << 28, K=8, N=8), _abi.MOE_EINVAL),
+    # one expert's weight matrix past 2^31 elements, a row wider than the limit
+    (dict(d=1 << 16, F=1 << 14), _abi.MOE_EINVAL),
+    (dict(d=_abi.MOE_MAX_WIDTH + 8, F=8), _abi.MOE_EINVAL),
+    (dict(F=_abi.MOE_MAX_WIDTH + 8, d=8), _abi.MOE_EINVAL),
+    # grouped-GEMM tile count past a 32-bit grid: 2^30 buffer rows of 2F = 2^15
+    (dict(T=1 << 27, K=8, N=8, ep_size=1, ep_rank=0, capacity=1 << 27, d=8, F=1 << 14),
+     _abi.MOE_EINVAL),
 ])
 def test_validation_rejects_bad_shapes(bad, code):
     s = moe.MoeShape(**{**BASE, **bad})
@@ -155,3 +162,24 @@ def test_buffer_rows_of_special_shapes():
     assert lib.moe_buffer_rows(ctypes.byref(cs)) == _abi.MOE_EINVAL
     with pytest.raises(moe.MoeError):
         moe.MoeShape(**{**BASE, "K": 0}).rows
+
+
+def test_validation_admits_the_bounds_themselves():
+    ok = [dict(d=_abi.MOE_MAX_WIDTH, F=8), dict(F=_abi.MOE_MAX_WIDTH, d=8),
+          dict(d=1 << 16, F=(1 << 14) - 8)]
+    for kw in ok:
+        assert moe.moe_validate_shape(moe.MoeShape(**{**BASE, **kw})) == 0, kw
+
+
+def test_backward_refuses_to_follow_the_mx_forward():
+    """MoELayer.backward differentiates the BF16 forward only: after the MXFP8
+    forward (or before any forward) it raises before enqueueing anything."""
+    import torch
+    s = moe.MoeShape(**BASE)
+    layer = moe.MoELayer(s, device="cpu")   # host buffers: nothing is launched
+    dout = torch.zeros(s.T, s.d, dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError, match="BF16 forward"):
+        layer.backward(dout, None, None)
+    layer.last_forward = "mx"
+    with pytest.raises(RuntimeError, match="inference-only"):
+        layer.backward(dout, None, None)

@@ -210,3 +210,86 @@ def test_largest_capacity_routes_like_capacity_t():
     assert bool(is_poison(layer.buf[n:]).all()) and bool(is_poison(layer.y[n:]).all())
     assert_rows_close(to_np(layer.y[:n]), ref["y"][:n], tol_of("bf16"), "y")
     assert_rows_close(to_np(layer.out), ref["out"], tol_of("bf16"), "out")
+
+
+def test_row_buffers_past_2_32_elements():
+    """A dropless layer with every route kept (K = N = 8, one rank): 655,360
+    buffer rows of d = 8192, 5.4e9 elements per row buffer. The GEMMs address
+    a tile's rows with 32-bit offsets from a 64-bit base at the tile's first
+    row, so rows past element 2^32 must come out right: the rows around that
+    boundary and the last rows of the last expert (H, Y, dX rows, the MXFP8
+    H codes), and the outputs and input gradients of the last tokens, each
+    recomputed by the oracle."""
+    cfg = LayerConfig("rows_past_2_32", T=81920, d=8192, N=8, K=8, F=128, cf=Fraction(1),
+                      dtype="bf16", seed=47, dropless=True)
+    print("[case] row buffers past 2^32 elements", flush=True)
+    shape = moe.MoeShape.from_config(cfg)
+    T, d, K = cfg.T, cfg.d, cfg.K
+    assert shape.rows == T * K and shape.rows * d > (1 << 32)
+    inp = make_inputs(cfg, "cuda")
+    layer = moe.MoELayer(shape, "cuda")
+    layer.forward(inp.logits, inp.x, inp.w_gu, inp.w_d)
+    dout = torch.randn(T, d, generator=torch.Generator("cuda").manual_seed(48),
+                       device="cuda").to(torch.bfloat16)
+    dx, _, _, _ = layer.backward(dout, inp.w_gu, inp.w_d)
+    torch.cuda.synchronize()
+    ref = oracle_route(cfg, inp.logits.cpu())
+    assert_route_fields(layer.route, ref, ("counts", "offsets", "dest_rank", "dest_row"))
+    off = ref["offsets"][0]
+    assert list(off) == [e * T for e in range(cfg.N + 1)]
+    # rows straddling element 2^32 (expert 6) and the last rows (expert 7)
+    edge = (1 << 32) // d
+    rows = np.concatenate([np.arange(edge - 40, edge + 40), np.arange(shape.rows - 64, shape.rows)])
+    src = ref["row_src"][rows]
+    x64 = inp.x[torch.from_numpy(src // K).cuda()].cpu().double().numpy()
+    tol = tol_of("bf16")
+    w = {j: (inp.w_gu[j].cpu().double().numpy(), inp.w_d[j].cpu().double().numpy())
+         for j in (6, 7)}
+    Hs, Ys, dXs = [], [], []
+    for i, r in enumerate(rows):
+        j = int(r // T)
+        t, k = int(src[i] // K), int(src[i] % K)
+        H, Y = orc.expert_ffn_rows(x64[i:i + 1], *w[j], "bf16")
+        dY = orc.round_to(float(ref["topk_w"][t, k]) * dout[t:t + 1].cpu().double().numpy(),
+                          "bf16")
+        dXs.append(orc.expert_ffn_bwd_rows(x64[i:i + 1], *w[j], H, dY, "bf16")["dx"][0])
+        Hs.append(H[0])
+        Ys.append(Y[0])
+    sel = torch.from_numpy(rows).cuda()
+    assert_rows_close(to_np(layer.h[sel]), np.array(Hs), tol, "h past 2^32")
+    assert_rows_close(to_np(layer.y[sel]), np.array(Ys), tol, "y past 2^32")
+    assert_rows_close(to_np(layer.dx_rows[sel]), np.array(dXs), tol, "dx_rows past 2^32")
+    # the last tokens: all 8 routes of each, output and input gradient
+    toks = np.arange(T - 16, T)
+    y_rows, dx_ref = {}, np.zeros((len(toks), d))
+    wall = {j: (inp.w_gu[j].cpu().double().numpy(), inp.w_d[j].cpu().double().numpy())
+            for j in range(cfg.N)}
+    xt = inp.x[T - 16:].cpu().double().numpy()
+    dt = dout[T - 16:].cpu().double().numpy()
+    for i, t in enumerate(toks):
+        for k in range(K):
+            r = int(ref["dest_row"][t, k])
+            j = r // T
+            H, Y = orc.expert_ffn_rows(xt[i:i + 1], *wall[j], "bf16")
+            y_rows[r] = Y[0]
+            dY = orc.round_to(float(ref["topk_w"][t, k]) * dt[i:i + 1], "bf16")
+            dx_ref[i] += orc.expert_ffn_bwd_rows(xt[i:i + 1], *wall[j], H, dY, "bf16")["dx"][0]
+    expect = orc.combine_tokens(toks, lambda r: y_rows[r], ref["dest_rank"], ref["dest_row"],
+                                ref["topk_w"], 0, d, "bf16")
+    tsel = torch.from_numpy(toks).cuda()
+    assert_rows_close(to_np(layer.out[tsel]), expect, tol, "out past 2^32")
+    assert_rows_close(to_np(dx[tsel]), orc.round_to(dx_ref, "bf16"), tol, "dx past 2^32")
+    # MXFP8 forward on the same shape: quantize-on-dispatch rows past 2^32 bytes
+    mxw = moe.MxWeights.from_bf16(inp.w_gu, inp.w_d)
+    layer.forward_mx(inp.logits, inp.x, mxw)
+    torch.cuda.synchronize()
+    eq, es = orc.mx_quantize(x64)
+    np.testing.assert_array_equal(layer.qbuf[sel].cpu().numpy(), eq)
+    np.testing.assert_array_equal(layer.sbuf[sel].cpu().numpy(), es)
+    wq = {j: orc.mx_quantize(w[j][0]) + orc.mx_quantize(w[j][1]) for j in w}
+    Yq = [orc.expert_ffn_mx_rows(eq[i:i + 1], es[i:i + 1], *wq[int(r // T)])[2][0]
+          for i, r in enumerate(rows)]
+    # the MXFP8 end-to-end bar (H codes may flip at rounding boundaries)
+    assert_rows_close(to_np(layer.y[sel]), np.array(Yq), 5e-2, "mx y past 2^32")
+    del layer, inp, dout, dx
+    torch.cuda.empty_cache()

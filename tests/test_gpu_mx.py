@@ -181,6 +181,7 @@ def test_expert_up_down_mx_stages(cfg):
 # 5e-2 and the median row within 1e-2 (a scale or layout mistake moves the
 # median by orders of magnitude, isolated flips move single rows).
 E2E_ROW, E2E_MEDIAN = 5e-2, 1e-2
+MX_TOKENS = 512
 MX_LAYER = MX_SMALL[:2] + [MX_SMALL[2].with_(name="mx_zipf_drops_256", d=256, F=256),
                            MX_SMALL[3].with_(name="mx_many_experts_256", d=256, F=256),
                            MX_SMALL[4].with_(name="mx_zipf_dropless_256", d=256, F=256)]
@@ -228,9 +229,9 @@ def test_layer_mx_matches_oracle(cfg):
                                   "zipf_dropless_bf16"])
 def test_full_config_mx(name):
     """Full workload sizes: MoELayer.forward_mx; routing and quantize-on-dispatch
-    checked on sampled rows bit-exactly, the expert outputs of sampled rows of
-    sampled experts and the combined output of sampled tokens recomputed one
-    by one by the oracle."""
+    checked bit-exactly (the whole route map, 256+ sampled dispatch rows),
+    every row of 3 experts (first, last, one seeded pick) and 512 whole
+    tokens of the combined output recomputed by the oracle."""
     cfg = CONFIGS[name]
     print(f"[case] full mx {name}", flush=True)
     inp = make_inputs(cfg, "cuda")
@@ -271,24 +272,28 @@ def test_full_config_mx(name):
         np.testing.assert_array_equal(_u8(mxw.w_gu_q[j]), gq)
         np.testing.assert_array_equal(_u8(mxw.w_d_s[j]), ds)
         a, b = int(off[j]), int(off[j + 1])
-        rr = np.unique(np.concatenate([[a, b - 1], rng.integers(a, b, 12)]))
-        Xq, Xs = orc.mx_quantize(x[ref["row_src"][rr] // K])
+        Xq, Xs = orc.mx_quantize(x[ref["row_src"][a:b] // K])
         Hq, Hs, Y = orc.expert_ffn_mx_rows(Xq, Xs, gq, gs, dq, ds)
-        s2 = torch.from_numpy(rr).cuda()
-        _check_h(_u8(layer.h_q[s2]), _u8(layer.h_s[s2]), Hq, Hs, f"h expert {j}")
-        assert_rows_close(to_np(layer.y[s2]), Y, E2E_ROW, f"y expert {j}")
-    # combined output on sampled tokens
-    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 6)]))
-
-    def y_of_row(row):
-        j = int(np.searchsorted(off, row, side="right") - 1)
-        gq, gs, dq, ds = wq(j)
-        Xq, Xs = orc.mx_quantize(x[int(ref["row_src"][row] // K)][None])
-        return orc.expert_ffn_mx_rows(Xq, Xs, gq, gs, dq, ds)[2][0]
-
-    expect = orc.combine_tokens(toks, y_of_row, ref["dest_rank"], ref["dest_row"], ref["topk_w"],
-                                cfg.ep_rank, d, "bf16")
-    assert_rows_close(to_np(layer.out[torch.from_numpy(toks).cuda()]), expect, E2E_ROW, "out")
+        _check_h(_u8(layer.h_q[a:b]), _u8(layer.h_s[a:b]), Hq, Hs, f"h expert {j}")
+        _check_e2e(to_np(layer.y[a:b]), Y, f"y expert {j}")
+    # combined output of 512 whole tokens: each kept local route's expert row
+    # recomputed by the oracle (grouped by expert), then the oracle's combine
+    toks = np.unique(np.concatenate([[0, cfg.T - 1],
+                                     rng.choice(cfg.T, size=MX_TOKENS - 2, replace=False)]))
+    assert len(toks) == MX_TOKENS
+    dr, drow = ref["dest_rank"][toks], ref["dest_row"][toks]
+    rows = np.unique(drow[(dr == cfg.ep_rank) & (drow >= 0)])
+    expert_of = np.searchsorted(off, rows, side="right") - 1
+    y_rows = {}
+    for j in np.unique(expert_of):
+        rj = rows[expert_of == j]
+        gq, gs = orc.mx_quantize(_f64(inp.w_gu[int(j)]))
+        dq, ds = orc.mx_quantize(_f64(inp.w_d[int(j)]))
+        Xq, Xs = orc.mx_quantize(x[ref["row_src"][rj] // K])
+        y_rows.update(zip(rj.tolist(), orc.expert_ffn_mx_rows(Xq, Xs, gq, gs, dq, ds)[2]))
+    expect = orc.combine_tokens(toks, lambda r: y_rows[r], ref["dest_rank"], ref["dest_row"],
+                                ref["topk_w"], cfg.ep_rank, d, "bf16")
+    _check_e2e(to_np(layer.out[torch.from_numpy(toks).cuda()]), expect, "out")
 
 
 def test_mx_calls_reject_what_they_do_not_cover():
