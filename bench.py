@@ -121,8 +121,8 @@ def time_mx(args, layer, inp, stream, torch) -> dict:
     Not part of ``value``."""
     import combine_top_softmax_amd as moe
     s = layer.shape
-    if s.dtype != "bf16" or s.d % 128 or s.F % 128:
-        return {"skipped": "the MXFP8 path needs a bf16 layer with d and F multiples of 128"}
+    if s.dtype != "bf16" or s.d % 64 or s.F % 64:
+        return {"skipped": "the MXFP8 path needs a bf16 layer with d and F multiples of 64"}
     mxw = moe.MxWeights.from_bf16(inp.w_gu, inp.w_d)
     layer.alloc_mx("cuda")
 

@@ -26,7 +26,8 @@ __all__ = [
     "moe_expert_ffn_bwd_data", "moe_expert_ffn_bwd_weight", "moe_expert_up_save_gu",
     "moe_expert_ffn_bwd_data_saved_gu",
     "moe_dispatch_bwd", "moe_route_bwd", "moe_mx_quantize_rows", "moe_dispatch_rows_mx",
-    "moe_expert_up_mx", "moe_expert_down_mx", "MxWeights", "moe_strerror", "moe_validate_shape",
+    "moe_expert_up_mx", "moe_expert_down_mx", "MxWeights", "mx_scale_cols", "moe_strerror",
+    "moe_validate_shape",
 ]
 
 
@@ -362,16 +363,24 @@ def moe_route_bwd(shape: MoeShape, topk_idx, topk_w, dw, dlogits, stream=None) -
 
 
 # ----------------------------------------------------------------- MXFP8
+def mx_scale_cols(cols: int) -> int:
+    """Bytes per MX scale row of ``cols`` elements: cols / 32 block scales
+    rounded up to a multiple of 4 (the rows start 4-byte aligned)."""
+    return (cols // 32 + 3) // 4 * 4
+
+
 def moe_mx_quantize_rows(src, qdata, scales, stream=None) -> None:
     """MX-quantize the rows of a bf16 tensor along its last dimension (a
-    multiple of 32): qdata uint8 of src's shape, scales uint8 [..., cols/32]."""
+    multiple of 32): qdata uint8 of src's shape, scales uint8
+    [..., mx_scale_cols(cols)] (the first cols/32 bytes of a row are its
+    scales)."""
     if not isinstance(src, torch.Tensor) or src.dtype != torch.bfloat16 or src.dim() < 1:
         raise ValueError("src must be a bf16 tensor")
     cols = src.shape[-1]
     rows = src.numel() // cols if cols else 0
     _need(src, "src", tuple(src.shape), torch.bfloat16)
     _need(qdata, "qdata", tuple(src.shape), torch.uint8)
-    _need(scales, "scales", tuple(src.shape[:-1]) + (cols // 32,), torch.uint8)
+    _need(scales, "scales", tuple(src.shape[:-1]) + (mx_scale_cols(cols),), torch.uint8)
     rc = _abi.load().moe_mx_quantize_rows(rows, cols, _ptr(src), _ptr(qdata), _ptr(scales),
                                           _stream(stream))
     _abi.check("moe_mx_quantize_rows", rc)
@@ -383,7 +392,7 @@ def moe_dispatch_rows_mx(shape: MoeShape, x, dest_rank, dest_row, qbuf, sbuf,
     _need(dest_rank, "dest_rank", (shape.T, shape.K), torch.int32)
     _need(dest_row, "dest_row", (shape.T, shape.K), torch.int32)
     _need(qbuf, "qbuf", (shape.rows, shape.d), torch.uint8)
-    _need(sbuf, "sbuf", (shape.rows, shape.d // 32), torch.uint8)
+    _need(sbuf, "sbuf", (shape.rows, mx_scale_cols(shape.d)), torch.uint8)
     rc = _abi.load().moe_dispatch_rows_mx(ctypes.byref(shape.c()), _ptr(x), _ptr(dest_rank),
                                           _ptr(dest_row), _ptr(qbuf), _ptr(sbuf), _stream(stream))
     _abi.check("moe_dispatch_rows_mx", rc)
@@ -393,12 +402,12 @@ def moe_expert_up_mx(shape: MoeShape, qbuf, sbuf, offsets, w_gu_q, w_gu_s, h_q, 
                      stream=None) -> None:
     u8 = torch.uint8
     _need(qbuf, "qbuf", (shape.rows, shape.d), u8)
-    _need(sbuf, "sbuf", (shape.rows, shape.d // 32), u8)
+    _need(sbuf, "sbuf", (shape.rows, mx_scale_cols(shape.d)), u8)
     _ffn_checks(shape, offsets)
     _need(w_gu_q, "w_gu_q", (shape.E_L, 2 * shape.F, shape.d), u8)
-    _need(w_gu_s, "w_gu_s", (shape.E_L, 2 * shape.F, shape.d // 32), u8)
+    _need(w_gu_s, "w_gu_s", (shape.E_L, 2 * shape.F, mx_scale_cols(shape.d)), u8)
     _need(h_q, "h_q", (shape.rows, shape.F), u8)
-    _need(h_s, "h_s", (shape.rows, shape.F // 32), u8)
+    _need(h_s, "h_s", (shape.rows, mx_scale_cols(shape.F)), u8)
     rc = _abi.load().moe_expert_up_mx(ctypes.byref(shape.c()), _ptr(qbuf), _ptr(sbuf),
                                       _ptr(offsets), _ptr(w_gu_q), _ptr(w_gu_s), _ptr(h_q),
                                       _ptr(h_s), _stream(stream))
@@ -408,10 +417,10 @@ def moe_expert_up_mx(shape: MoeShape, qbuf, sbuf, offsets, w_gu_q, w_gu_s, h_q, 
 def moe_expert_down_mx(shape: MoeShape, h_q, h_s, offsets, w_d_q, w_d_s, y, stream=None) -> None:
     u8 = torch.uint8
     _need(h_q, "h_q", (shape.rows, shape.F), u8)
-    _need(h_s, "h_s", (shape.rows, shape.F // 32), u8)
+    _need(h_s, "h_s", (shape.rows, mx_scale_cols(shape.F)), u8)
     _ffn_checks(shape, offsets)
     _need(w_d_q, "w_d_q", (shape.E_L, shape.d, shape.F), u8)
-    _need(w_d_s, "w_d_s", (shape.E_L, shape.d, shape.F // 32), u8)
+    _need(w_d_s, "w_d_s", (shape.E_L, shape.d, mx_scale_cols(shape.F)), u8)
     _need(y, "y", (shape.rows, shape.d), torch.bfloat16)
     rc = _abi.load().moe_expert_down_mx(ctypes.byref(shape.c()), _ptr(h_q), _ptr(h_s),
                                         _ptr(offsets), _ptr(w_d_q), _ptr(w_d_s), _ptr(y),
@@ -423,9 +432,9 @@ def moe_expert_down_mx(shape: MoeShape, h_q, h_s, offsets, w_d_q, w_d_s, y, stre
 class MxWeights:
     """Expert weights quantized once along their contraction dimension."""
     w_gu_q: torch.Tensor   # [E_L, 2F, d] uint8
-    w_gu_s: torch.Tensor   # [E_L, 2F, d/32] uint8
+    w_gu_s: torch.Tensor   # [E_L, 2F, mx_scale_cols(d)] uint8
     w_d_q: torch.Tensor    # [E_L, d, F] uint8
-    w_d_s: torch.Tensor    # [E_L, d, F/32] uint8
+    w_d_s: torch.Tensor    # [E_L, d, mx_scale_cols(F)] uint8
 
     @classmethod
     def from_bf16(cls, w_gu: torch.Tensor, w_d: torch.Tensor, stream=None) -> "MxWeights":
@@ -433,9 +442,9 @@ class MxWeights:
         E_L, F2, d = w_gu.shape
         F = F2 // 2
         q = cls(torch.empty(E_L, F2, d, dtype=u8, device=w_gu.device),
-                torch.empty(E_L, F2, d // 32, dtype=u8, device=w_gu.device),
+                torch.empty(E_L, F2, mx_scale_cols(d), dtype=u8, device=w_gu.device),
                 torch.empty(E_L, d, F, dtype=u8, device=w_gu.device),
-                torch.empty(E_L, d, F // 32, dtype=u8, device=w_gu.device))
+                torch.empty(E_L, d, mx_scale_cols(F), dtype=u8, device=w_gu.device))
         moe_mx_quantize_rows(w_gu, q.w_gu_q, q.w_gu_s, stream)
         moe_mx_quantize_rows(w_d, q.w_d_q, q.w_d_s, stream)
         return q
@@ -501,9 +510,9 @@ class MoELayer:
         s = self.shape
         u8 = torch.uint8
         self.qbuf = torch.empty(s.rows, s.d, dtype=u8, device=device)
-        self.sbuf = torch.empty(s.rows, s.d // 32, dtype=u8, device=device)
+        self.sbuf = torch.empty(s.rows, mx_scale_cols(s.d), dtype=u8, device=device)
         self.h_q = torch.empty(s.rows, s.F, dtype=u8, device=device)
-        self.h_s = torch.empty(s.rows, s.F // 32, dtype=u8, device=device)
+        self.h_s = torch.empty(s.rows, mx_scale_cols(s.F), dtype=u8, device=device)
 
     def dispatch_mx_step(self, x, stream=None):
         r = self.route

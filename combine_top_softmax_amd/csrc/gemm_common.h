@@ -110,18 +110,23 @@ struct ExpertTile {
   bool valid;
 };
 
-__device__ __forceinline__ ExpertTile find_expert_tile(const int32_t *__restrict__ off, int E_L,
-                                                       int bm, int n_tiles_n) {
-  ExpertTile t;
-  t.valid = false;
-  const ExpertChunk c0 = expert_chunk(off, E_L, 0, bm);
+// m-tiles (bm rows each) of all local experts: the tile count is this times
+// the n-tiles. The c0 chunk (experts 0..63) is returned for reuse.
+__device__ __forceinline__ int count_m_tiles(const int32_t *__restrict__ off, int E_L, int bm,
+                                             ExpertChunk &c0) {
+  c0 = expert_chunk(off, E_L, 0, bm);
   int total_m = c0.tot;
   for (int c = 64; c < E_L; c += 64) total_m += expert_chunk(off, E_L, c, bm).tot;
-  const int total = total_m * n_tiles_n;
-  const int q = (total + kNumXcd - 1) / kNumXcd;
-  const int slot = blockIdx.x / kNumXcd;
-  const int L = (blockIdx.x % kNumXcd) * q + slot;
-  if (slot >= q || L >= total) return t;
+  return total_m;
+}
+
+// Tile L (< total) of the expert-by-expert numbering: its expert, the
+// expert's m-tile run and rows. c0: the first chunk, as count_m_tiles read it.
+__device__ __forceinline__ ExpertTile expert_tile_at(const int32_t *__restrict__ off, int E_L,
+                                                     int bm, int n_tiles_n, int L,
+                                                     const ExpertChunk &c0) {
+  ExpertTile t;
+  t.valid = false;
   const int m_glob = L / n_tiles_n;
   int run = 0;
   for (int c = 0; c < E_L; c += 64) {
@@ -145,6 +150,19 @@ __device__ __forceinline__ ExpertTile find_expert_tile(const int32_t *__restrict
     run += ch.tot;
   }
   return t;
+}
+
+__device__ __forceinline__ ExpertTile find_expert_tile(const int32_t *__restrict__ off, int E_L,
+                                                       int bm, int n_tiles_n) {
+  ExpertTile t;
+  t.valid = false;
+  ExpertChunk c0;
+  const int total = count_m_tiles(off, E_L, bm, c0) * n_tiles_n;
+  const int q = (total + kNumXcd - 1) / kNumXcd;
+  const int slot = blockIdx.x / kNumXcd;
+  const int L = (blockIdx.x % kNumXcd) * q + slot;
+  if (slot >= q || L >= total) return t;
+  return expert_tile_at(off, E_L, bm, n_tiles_n, L, c0);
 }
 
 // Row-mode tiles: m-tile by m-tile, its n_tiles_n n-tiles consecutive.

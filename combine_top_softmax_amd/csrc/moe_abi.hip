@@ -262,7 +262,9 @@ static int check_mx_shape(const moe_shape_t *s) {
   const int rc = check_shape(s);
   if (rc != MOE_OK) return rc;
   if (s->dtype != MOE_BF16) return MOE_EDTYPE;
-  if (s->d % 128 != 0 || s->F % 128 != 0) return MOE_EINVAL;
+  // whole 64-element MFMA K slices in both GEMMs (d and F are each the
+  // contraction of one of them)
+  if (s->d % 64 != 0 || s->F % 64 != 0) return MOE_EINVAL;
   return MOE_OK;
 }
 

@@ -31,6 +31,11 @@ inline int64_t buffer_rows(const moe_shape_t &s) {
   return E_L * s.capacity < by_tok ? E_L * s.capacity : by_tok;
 }
 
+// Bytes between consecutive MX scale rows of `cols` elements: the cols / 32
+// block scales rounded up to a multiple of 4, so that every row's scales
+// start 4-byte aligned (the GEMMs load them as dwords).
+__host__ __device__ inline int mx_scale_row_bytes(int cols) { return ((cols >> 5) + 3) & ~3; }
+
 // Launchers (return MOE_OK or MOE_EHIP). Shapes are already validated.
 int launch_route(const moe_shape_t &s, const float *logits, const int32_t *ids_in,
                  const moe_route_out_t &o, void *ws, hipStream_t st);

@@ -92,7 +92,8 @@ __device__ __forceinline__ float amax8(const u32x4_t v) {
 // ------------------------------------------------------------ quantize rows
 // ROUTED: row t of x goes to every route with dest_rank == ep_rank, at
 // dest_row; else row r goes to row r (n_src rows). Row length d (bf16),
-// d % 32 == 0.
+// d % 32 == 0. Scale rows are mx_scale_row_bytes(d) bytes apart (the d / 32
+// scales, then pad bytes that are not written).
 template <bool ROUTED>
 __global__ __launch_bounds__(256) void k_quant_rows(
     const u32x4_t *__restrict__ x, const int32_t *__restrict__ dest_rank,
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(
   const int64_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= n_src) return;
   const int nvec = d >> 3;                 // 16-byte vectors per row
-  const int nblk = d >> 5;                 // scale bytes per row
+  const int nblk = mx_scale_row_bytes(d);  // scale row stride
   const u32x4_t *src = x + t * nvec;
   for (int seg = 0; seg < nvec; seg += 64) {
     const int c = seg + lane;
@@ -159,19 +160,29 @@ struct MxCtx {
   int sa_lds[mxg::TM], sb_lds[mxg::TN];
   int sw;
   uint32_t a_skip;            // A loads that feed only rows past the valid ones
+  int kdim;                   // K (bytes of a qdata row)
+  // half K step: bytes to take off a load's offset so that it reads chunk
+  // (logical chunk & 3), one of the 64 valid bytes: 64 if the load's logical
+  // chunk pch ^ swz(r) is 4..7, else 0. With 8 rows per load instruction, bit
+  // 2 of swz(r) is bit 2 of the lane's row in the instruction, so the value
+  // is the same for every A and B load of the lane.
+  uint32_t hadj;
 };
 
 __device__ __forceinline__ void mx_issue(const MxCtx &c, int k0, int wv, uint32_t stage) {
+  const uint32_t hm = k0 + mxg::BK > c.kdim ? ~0u : 0u;   // a half step's loads
 #pragma unroll
   for (int j = 0; j < mxg::SPW; ++j)
     dma4(c.S[j] + (uint32_t)(c.s_off[j] + (k0 >> 5)), stage + c.s_dst[j]);
 #pragma unroll
   for (int i = 0; i < mxg::NA; ++i)
     if (!((c.a_skip >> i) & 1))
-      dma16(c.A + (uint32_t)(c.a_off[i] + k0), stage + (wv * mxg::NA + i) * 1024);
+      dma16(c.A + (uint32_t)(c.a_off[i] + k0 - (c.hadj & hm)),
+            stage + (wv * mxg::NA + i) * 1024);
 #pragma unroll
   for (int i = 0; i < mxg::NB; ++i)
-    dma16(c.W + (uint32_t)(c.b_off[i] + k0), stage + mxg::A_BYTES + (wv * mxg::NB + i) * 1024);
+    dma16(c.W + (uint32_t)(c.b_off[i] + k0 - (c.hadj & hm)),
+          stage + mxg::A_BYTES + (wv * mxg::NB + i) * 1024);
 }
 
 // One main-loop step: 2 x 8 scaled MFMAs from `rd`, the direct loads of the
@@ -183,7 +194,9 @@ __device__ __forceinline__ void mx_issue(const MxCtx &c, int k0, int wv, uint32_
 // the row of the lane's fragment).
 // VT: this wave's 32-row MFMA tiles that hold valid rows (fewer than TM on an
 // expert's last m-tile: the others' MFMAs and A fragment reads are dropped).
-template <int VT>
+// KSE: the K sub-steps this step runs (1 for a half step); LOADS: whether it
+// issues the next step's loads (a half step is the last one and issues none).
+template <int VT, int KSE = mxg::KS, bool LOADS = true>
 __device__ __forceinline__ void mx_step(const MxCtx &c, int k0, int wv,
                                         uint32_t ld, const uint8_t *__restrict__ rd,
                                         int g, f32x16_t (&acc)[mxg::TM][mxg::TN]) {
@@ -192,12 +205,14 @@ __device__ __forceinline__ void mx_step(const MxCtx &c, int k0, int wv,
   constexpr int GAP = MF / (2 * L) > 0 ? MF / (2 * L) : 1;
   // k0: the K offset (bytes) of the step loaded into `ld` (the caller repeats
   // the last step on the last iteration: no branch inside the step)
+  const uint32_t hm = k0 + mxg::BK > c.kdim ? ~0u : 0u;   // loads of a half step
   auto issue_one = [&](int d) {
     if (d < mxg::NA) {
       if (VT == mxg::TM || !((c.a_skip >> d) & 1))
-        dma16(c.A + (uint32_t)(c.a_off[d] + k0), ld + (wv * mxg::NA + d) * 1024);
+        dma16(c.A + (uint32_t)(c.a_off[d] + k0 - (c.hadj & hm)),
+              ld + (wv * mxg::NA + d) * 1024);
     } else if (d < mxg::L)
-      dma16(c.W + (uint32_t)(c.b_off[d - mxg::NA] + k0),
+      dma16(c.W + (uint32_t)(c.b_off[d - mxg::NA] + k0 - (c.hadj & hm)),
             ld + mxg::A_BYTES + (wv * mxg::NB + (d - mxg::NA)) * 1024);
     else {
       const int j = d - mxg::L;
@@ -236,7 +251,7 @@ __device__ __forceinline__ void mx_step(const MxCtx &c, int k0, int wv,
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int ks = 0; ks < mxg::KS; ++ks) {
+  for (int ks = 0; ks < KSE; ++ks) {
     const int cur = ks & 1;
 #pragma unroll
     for (int q = 0; q < mxg::TM * mxg::TN; ++q) {
@@ -250,21 +265,26 @@ __device__ __forceinline__ void mx_step(const MxCtx &c, int k0, int wv,
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               fra[i], frb[cur][j], acc[i][j], 0, 0, 2, (int)sa[i], 2, (int)sb[j]);
       }
-      if (ks + 1 < mxg::KS) {
+      if (ks + 1 < KSE) {
         if (q < mxg::TN) frb[cur ^ 1][q] = frag(c.fb[q], ks + 1);
         if (j == mxg::TN - 1 && i < VT) fra[i] = frag(c.fa[i], ks + 1);
       }
-      if (gi % GAP == 0 && gi / GAP < L) issue_one(gi / GAP);
+      if (LOADS && gi % GAP == 0 && gi / GAP < L) issue_one(gi / GAP);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-// A: qdata rows [rows, Kdim] with scales As [rows, Kdim/32]; W: expert weights
+// A: qdata rows [rows, Kdim] with scales As [rows, SK]; W: expert weights
 // [E_L, Nw, Kdim] (Nw = 2 Nout for GATE_UP: gate rows then up rows) with
-// scales Ws [E_L, Nw, Kdim/32]. GATE_UP: H = silu(G) * U (Nout = F columns)
-// rounded to bf16, written as qdata OutQ [rows, Nout] and scales OutS
-// [rows, Nout/32]; else Y = A W^T in bf16 (OutY [rows, Nout]).
+// scales Ws [E_L, Nw, SK]; SK = mx_scale_row_bytes(Kdim). GATE_UP: H =
+// silu(G) * U (Nout = F columns) rounded to bf16, written as qdata OutQ
+// [rows, Nout] and scales OutS [rows, mx_scale_row_bytes(Nout)]; else
+// Y = A W^T in bf16 (OutY [rows, Nout]). Kdim % 64 == 0: when Kdim % 128 ==
+// 64 the last K step is half a step (one 64-wide MFMA sub-step); its loads
+// read only the 64 valid bytes of each row (the other lanes load a valid
+// chunk again, into LDS bytes no MFMA reads) and the scale dword it reads
+// ends in two pad bytes of the scale row.
 template <bool GATE_UP>
 __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ W,
@@ -286,7 +306,7 @@ __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
   const int fr = lane & 31, g = lane >> 5;
   const int Nw = GATE_UP ? 2 * Nout : Nout;
   const int n0 = tl.n_idx * (GATE_UP ? mxg::BW / 2 : mxg::BW);
-  const int kb32 = Kdim >> 5;               // scale bytes per row
+  const int kb32 = mx_scale_row_bytes(Kdim);   // scale row stride
 
   MxCtx c;
   // A rows and their scale rows are addressed from the tile's first row
@@ -311,7 +331,10 @@ __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
       const int r = (wv * mxg::NB + i) * mxg::RPI + lrow;
       c.b_off[i] = (uint32_t)wrow_of(r) * (uint32_t)Kdim + ((pch ^ chunk_swz<8>(r)) << 4);
     }
+    static_assert(mxg::RPI == 8, "bit 2 of swz(r) is bit 2 of lrow");
+    c.hadj = ((pch ^ lrow) & 4) << 4;
   }
+  c.kdim = Kdim;
   c.sw = chunk_swz<8>(fr);
   // scale dwords of one step (4 blocks per row) through LDS, one dword per
   // lane: scale load u = wv * SPW + j takes A's rows 64u .. 64u+63 for u < 4,
@@ -357,7 +380,8 @@ __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = Kdim / mxg::BK;
+  const int nk = (Kdim + mxg::BK - 1) / mxg::BK;
+  const int nfull = Kdim / mxg::BK;           // nk - 1 when the last step is a half step
   // this wave's valid 32-row MFMA tiles and the A loads that feed only rows
   // past the last valid 32-row group of the tile (wave-uniform)
   const int nvalid = min(mxg::BM, tl.row_end - tl.row0);
@@ -371,16 +395,25 @@ __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
   mx_issue(c, 0, wv, smem_l);
   auto main_loop = [&](auto vt_tag) {
     constexpr int VT = decltype(vt_tag)::value;
-    for (int kb = 0; kb < nk; ++kb) {
+    for (int kb = 0; kb < nfull; ++kb) {
       wait_vmcnt<0>();                    // this wave's loads of step kb have landed ...
       __builtin_amdgcn_s_barrier();       // ... and every wave's
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       const uint32_t ld = smem_l + ((kb + 1) & 1) * mxg::STAGE;
       const uint8_t *rd = smem + (kb & 1) * mxg::STAGE;
-      // the next step's loads; the last iteration reloads its own step into
-      // the idle stage (in bounds, never read; drained before the epilogue)
+      // the next step's loads; the last step, when it is a full one, reloads
+      // its own step into the idle stage (in bounds, never read; drained
+      // before the epilogue)
       mx_step<VT>(c, min(kb + 1, nk - 1) * mxg::BK, wv, ld, rd, g, acc);
+    }
+    if (nfull < nk) {                     // the half step: loads nothing
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      mx_step<VT, 1, false>(c, nfull * mxg::BK, wv, smem_l, smem + (nfull & 1) * mxg::STAGE, g,
+                            acc);
     }
   };
   switch (vt) {
@@ -435,7 +468,7 @@ __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
   const int nrows = min(mxg::BM, tl.row_end - tl.row0);
   if constexpr (GATE_UP) {
     // H (bf16 in LDS) quantized along F: one 32-column block of a row per task
-    const int nblk_row = Nout >> 5;
+    const int nblk_row = mx_scale_row_bytes(Nout);
     for (int idx = tid; idx < mxg::BM * (OUTC / 32); idx += mxg::NT) {
       const int row = idx / (OUTC / 32), blk = idx % (OUTC / 32);
       if (row >= nrows || blk * 32 >= ncols) continue;

@@ -300,17 +300,23 @@ int moe_route_bwd(const moe_shape_t *shape, const int32_t *topk_idx, const float
  * moe_combine on the bf16 y).
  * Format (the OCP microscaling format the report cites): a row of n values is
  * stored as qdata [n] uint8 E4M3 codes (OCP "E4M3FN": bias 7, max 448, no
- * infinities) and scales [n/32] uint8 E8M0 codes (value 2^(code - 127)), one
+ * infinities) and n/32 uint8 E8M0 scale codes (value 2^(code - 127)), one
  * per 32 consecutive elements. A block's scale is 2^(floor(log2 amax) - 8);
  * each element is its value over the scale rounded to the nearest E4M3 value,
  * ties to the even code, saturating at 448, sign bit from the value's sign;
- * an all-zero block gets scale code 0. Requirements of the MX calls
+ * an all-zero block gets scale code 0. Scale arrays hold one row of
+ * SC(n) = 4*ceil(n/128) bytes per qdata row: the n/32 scales, then (when n is
+ * not a multiple of 128) two pad bytes that are never written and never
+ * affect a result, so that every scale row starts 4-byte aligned. Below,
+ * "[R, SC(n)]" is such an array. Requirements of the MX calls
  * (MOE_EDTYPE / MOE_EINVAL otherwise): dtype MOE_BF16, d and F multiples of
- * 128. Alignment: bf16 sources and qdata 16 bytes, scale arrays 4 bytes.
+ * 64 (whole 64-element K slices of the scaled MFMA; a contraction with
+ * K % 128 == 64 ends in a half K step). Alignment: bf16 sources and qdata
+ * 16 bytes, scale arrays 4 bytes.
  * ------------------------------------------------------------------------ */
 
 /* MX-quantize `rows` rows of `cols` bf16 values (cols % 32 == 0) along the row:
- * src [rows, cols] -> qdata [rows, cols], scales [rows, cols/32]. Used once per
+ * src [rows, cols] -> qdata [rows, cols], scales [rows, SC(cols)]. Used once per
  * weight refresh for the expert weights, along their contraction dimension:
  * W_gu as rows = E_L*2F, cols = d; W_d as rows = E_L*d, cols = F. */
 int moe_mx_quantize_rows(int64_t rows, int32_t cols, const void *src, uint8_t *qdata,
@@ -318,7 +324,7 @@ int moe_mx_quantize_rows(int64_t rows, int32_t cols, const void *src, uint8_t *q
 
 /* Quantize-on-dispatch: token row x[t] (bf16, [T,d]) MX-quantized along d;
  * its qdata and scale rows are written to row dest_row[t,k] of qbuf
- * [Rmax, d] and sbuf [Rmax, d/32] for every route with dest_rank[t,k] ==
+ * [Rmax, d] and sbuf [Rmax, SC(d)] for every route with dest_rank[t,k] ==
  * ep_rank. Rows after the packed prefix are not written. T == 0: MOE_OK. */
 int moe_dispatch_rows_mx(const moe_shape_t *shape, const void *x, const int32_t *dest_rank,
                          const int32_t *dest_row, uint8_t *qbuf, uint8_t *sbuf,
@@ -326,11 +332,11 @@ int moe_dispatch_rows_mx(const moe_shape_t *shape, const void *x, const int32_t 
 
 /* MXFP8 grouped expert FFN over the packed prefix (offsets as moe_expert_ffn):
  * up:   H = silu(X W_gate^T) * (X W_up^T) from qbuf/sbuf and the quantized
- *       W_gu (w_gu_q [E_L,2F,d], w_gu_s [E_L,2F,d/32]); fp32 accumulation, H
+ *       W_gu (w_gu_q [E_L,2F,d], w_gu_s [E_L,2F,SC(d)]); fp32 accumulation, H
  *       rounded to bf16 and MX-quantized along F into h_q [Rmax, F] and
- *       h_s [Rmax, F/32];
+ *       h_s [Rmax, SC(F)];
  * down: Y = H W_d^T from h_q/h_s and the quantized W_d (w_d_q [E_L,d,F],
- *       w_d_s [E_L,d,F/32]); Y [Rmax, d] bf16 (round to nearest even).
+ *       w_d_s [E_L,d,SC(F)]); Y [Rmax, d] bf16 (round to nearest even).
  * Only prefix rows are written. */
 int moe_expert_up_mx(const moe_shape_t *shape, const uint8_t *qbuf, const uint8_t *sbuf,
                      const int32_t *offsets, const uint8_t *w_gu_q, const uint8_t *w_gu_s,

@@ -61,7 +61,8 @@ def _record(what: str, rows: int, worst_row: float, worst_elem: float, max_abs: 
                        worst_elem_rel=worst_elem, max_abs_err=max_abs))
 
 
-def assert_rows_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str) -> float:
+def assert_rows_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str,
+                      elementwise: bool = True) -> float:
     """Element by element and row by row: for every element
     |got - ref| <= tol * max(|ref|, rms(ref row)), and for every row the
     relative L2 error ||got - ref|| / ||ref|| <= tol; rows that are exactly
@@ -69,7 +70,9 @@ def assert_rows_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str) -
     to the element itself, floored at the row's rms so that elements near
     zero (where a 1-ulp storage rounding is a large relative change) are held
     to the row's scale. Records the worst values (see REPORT) and returns the
-    worst per-row error."""
+    worst per-row error. elementwise=False records the element statistic
+    without holding it to tol (for results that inherit discrete differences
+    already validated upstream, such as MXFP8 code flips)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     if got.ndim == 1:
@@ -92,7 +95,7 @@ def assert_rows_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str) -
     worst, worst_e, max_abs = float(err.max()), float(elem.max()), float(diff.max())
     _record(what, len(ref), worst, worst_e, max_abs, tol)
     assert worst <= tol, f"{what}: worst per-row relative L2 error {worst:.3e} > {tol:.1e}"
-    if worst_e > tol:
+    if elementwise and worst_e > tol:
         i, j = np.unravel_index(int(np.argmax(elem)), elem.shape)
         raise AssertionError(
             f"{what}: element ({i}, {j}) of the nonzero rows off by {diff[i, j]:.3e} = "

@@ -107,7 +107,7 @@ def test_full_config_parity_experts_and_tokens(name):
     # whole tokens: each kept local route's expert row recomputed (grouped by
     # expert), then the oracle's combine of those rows
     toks = np.unique(np.concatenate([[0, cfg.T - 1],
-                                     rng.choice(cfg.T, size=N_TOKENS - 2, replace=False)]))
+                                     1 + rng.choice(cfg.T - 2, size=N_TOKENS - 2, replace=False)]))
     dr, drow = ref["dest_rank"][toks], ref["dest_row"][toks]
     rows = np.unique(drow[(dr == cfg.ep_rank) & (drow >= 0)])
     expert_of = np.searchsorted(off, rows, side="right") - 1

@@ -37,6 +37,10 @@ MX_SMALL = [
                 dtype="bf16", ep_size=2, ep_rank=1, seed=44),
     LayerConfig("mx_zipf_dropless", T=1500, d=128, N=24, K=3, F=128, cf=Fraction(1),
                 dtype="bf16", logits="zipf", zipf_s=1.1, seed=43, dropless=True),
+    # d and F = 64 (mod 128): both GEMMs end in a half K step, the scale rows
+    # carry pad bytes, the down GEMM's N tile is ragged
+    LayerConfig("mx_half_k", T=900, d=192, N=12, K=3, F=320, cf=Fraction(5, 4), dtype="bf16",
+                seed=46),
 ]
 
 
@@ -50,6 +54,25 @@ def _u8(t):
 
 def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _sc(cols):
+    """Bytes per scale row of `cols` elements (cols / 32 scales, padded to 4)."""
+    return moe.mx_scale_cols(cols)
+
+
+def _pad_s(a):
+    """An oracle scale array [..., n/32] widened to the library's scale rows;
+    the pad bytes are 0xFF (a NaN scale), which no result may depend on."""
+    w = _sc(a.shape[-1] * 32)
+    out = np.full(a.shape[:-1] + (w,), 0xFF, np.uint8)
+    out[..., :a.shape[-1]] = a
+    return out
+
+
+def _u8s(t, cols):
+    """The cols / 32 scale bytes of each row of a library scale tensor."""
+    return t.cpu().numpy()[..., :cols // 32]
 
 
 def _wide_rows(rows, cols, seed):
@@ -66,17 +89,18 @@ def _wide_rows(rows, cols, seed):
     return v.to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 32), (5, 96), (129, 2048), (64, 4096)])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (5, 96), (129, 2048), (64, 4096), (3, 2880)])
 def test_quantize_rows_bit_exact(rows, cols):
     print(f"[case] quantize rows {rows}x{cols}", flush=True)
     src = _wide_rows(rows, cols, seed=rows * 7 + cols)
     q = poison_(torch.empty(rows, cols, dtype=torch.uint8, device="cuda"))
-    s = poison_(torch.empty(rows, cols // 32, dtype=torch.uint8, device="cuda"))
+    s = poison_(torch.empty(rows, _sc(cols), dtype=torch.uint8, device="cuda"))
     moe.moe_mx_quantize_rows(src.cuda(), q, s)
     torch.cuda.synchronize()
     eq, es = orc.mx_quantize(_f64(src))
     np.testing.assert_array_equal(_u8(q), eq)
-    np.testing.assert_array_equal(_u8(s), es)
+    np.testing.assert_array_equal(_u8s(s, cols), es)
+    assert bool(is_poison(s[:, cols // 32:]).all()), "a pad byte of a scale row was written"
 
 
 @pytest.mark.parametrize("cfg", MX_SMALL, ids=lambda c: c.name)
@@ -86,7 +110,7 @@ def test_dispatch_mx_bit_exact(cfg):
     ref = oracle_route(cfg, inp.logits)
     shape = moe.MoeShape.from_config(cfg)
     qb = poison_(torch.empty(shape.rows, cfg.d, dtype=torch.uint8, device="cuda"))
-    sb = poison_(torch.empty(shape.rows, cfg.d // 32, dtype=torch.uint8, device="cuda"))
+    sb = poison_(torch.empty(shape.rows, _sc(cfg.d), dtype=torch.uint8, device="cuda"))
     moe.moe_dispatch_rows_mx(shape, inp.x.cuda(), _dev(ref["dest_rank"]), _dev(ref["dest_row"]),
                              qb, sb)
     torch.cuda.synchronize()
@@ -95,8 +119,9 @@ def test_dispatch_mx_bit_exact(cfg):
     n = int(ref["offsets"][cfg.ep_rank, -1])
     assert written[:n].all() and not written[n:].any()
     np.testing.assert_array_equal(_u8(qb[:n]), eq[:n])
-    np.testing.assert_array_equal(_u8(sb[:n]), es[:n])
+    np.testing.assert_array_equal(_u8s(sb[:n], cfg.d), es[:n])
     assert bool(is_poison(qb[n:]).all()) and bool(is_poison(sb[n:]).all())
+    assert bool(is_poison(sb[:, cfg.d // 32:]).all())
 
 
 # The scaled MFMA does not accumulate as exactly as fp32 FMAs: measured on the
@@ -150,9 +175,9 @@ def test_expert_up_down_mx_stages(cfg):
     off = ref["offsets"][cfg.ep_rank]
     n = int(off[-1])
     hq = poison_(torch.empty(shape.rows, F, dtype=torch.uint8, device="cuda"))
-    hs = poison_(torch.empty(shape.rows, F // 32, dtype=torch.uint8, device="cuda"))
-    moe.moe_expert_up_mx(shape, _dev(qb), _dev(sb), _dev(ref["offsets"]), _dev(gq), _dev(gs),
-                         hq, hs)
+    hs = poison_(torch.empty(shape.rows, _sc(F), dtype=torch.uint8, device="cuda"))
+    moe.moe_expert_up_mx(shape, _dev(qb), _dev(_pad_s(sb)), _dev(ref["offsets"]), _dev(gq),
+                         _dev(_pad_s(gs)), hq, hs)
     # the down GEMM gets the oracle's H, so each stage is judged on its own
     eHq = np.zeros((shape.rows, F), np.uint8)
     eHs = np.zeros((shape.rows, F // 32), np.uint8)
@@ -163,13 +188,14 @@ def test_expert_up_down_mx_stages(cfg):
             eHq[a:b], eHs[a:b] = orc.expert_up_mx_rows(qb[a:b], sb[a:b], gq[j], gs[j])
             eY[a:b] = orc.expert_down_mx_rows(eHq[a:b], eHs[a:b], dq[j], ds[j])
     y = poison_(torch.empty(shape.rows, d, dtype=torch.bfloat16, device="cuda"))
-    moe.moe_expert_down_mx(shape, _dev(eHq), _dev(eHs), _dev(ref["offsets"]), _dev(dq), _dev(ds),
-                           y)
+    moe.moe_expert_down_mx(shape, _dev(eHq), _dev(_pad_s(eHs)), _dev(ref["offsets"]), _dev(dq),
+                           _dev(_pad_s(ds)), y)
     torch.cuda.synchronize()
     if n > 0:
-        _check_h(_u8(hq[:n]), _u8(hs[:n]), eHq[:n], eHs[:n], "h")
+        _check_h(_u8(hq[:n]), _u8s(hs[:n], F), eHq[:n], eHs[:n], "h")
         assert_rows_close(to_np(y[:n]), eY[:n], 2e-2, "y")
     assert bool(is_poison(hq[n:]).all()) and bool(is_poison(hs[n:]).all())
+    assert bool(is_poison(hs[:, F // 32:]).all())
     assert bool(is_poison(y[n:]).all())
 
 
@@ -182,13 +208,19 @@ def test_expert_up_down_mx_stages(cfg):
 # median by orders of magnitude, isolated flips move single rows).
 E2E_ROW, E2E_MEDIAN = 5e-2, 1e-2
 MX_TOKENS = 512
+_WQ_CACHE = {}   # oracle-quantized expert weights, shared by workloads with equal draws
 MX_LAYER = MX_SMALL[:2] + [MX_SMALL[2].with_(name="mx_zipf_drops_256", d=256, F=256),
                            MX_SMALL[3].with_(name="mx_many_experts_256", d=256, F=256),
-                           MX_SMALL[4].with_(name="mx_zipf_dropless_256", d=256, F=256)]
+                           MX_SMALL[4].with_(name="mx_zipf_dropless_256", d=256, F=256),
+                           MX_SMALL[5]]
 
 
 def _check_e2e(got, ref, what):
-    worst = assert_rows_close(got, ref, E2E_ROW, what)
+    # row-level bars only: a flipped H code moves every element of its row's Y
+    # by step * W_d[:, f], so single elements can sit far past a row-level
+    # error when a few flips line up in one column (measured: 5.8% of the
+    # element with a 1.9% row error on an F = 256 layer)
+    worst = assert_rows_close(got, ref, E2E_ROW, what, elementwise=False)
     nz = ~np.all(ref == 0, axis=1)
     err = np.linalg.norm(got[nz] - ref[nz], axis=1) / np.linalg.norm(ref[nz], axis=1)
     assert np.median(err) <= E2E_MEDIAN, f"{what}: median row error {np.median(err):.3e}"
@@ -212,21 +244,22 @@ def test_layer_mx_matches_oracle(cfg):
                            cfg.K, cfg.capacity, cfg.ep_size, cfg.ep_rank)
     check_route(layer.route, ref, shape)
     np.testing.assert_array_equal(_u8(mxw.w_gu_q), ref["w_gu_q"])
-    np.testing.assert_array_equal(_u8(mxw.w_gu_s), ref["w_gu_s"])
+    np.testing.assert_array_equal(_u8s(mxw.w_gu_s, cfg.d), ref["w_gu_s"])
     np.testing.assert_array_equal(_u8(mxw.w_d_q), ref["w_d_q"])
-    np.testing.assert_array_equal(_u8(mxw.w_d_s), ref["w_d_s"])
+    np.testing.assert_array_equal(_u8s(mxw.w_d_s, cfg.F), ref["w_d_s"])
     n = int(ref["offsets"][cfg.ep_rank, -1])
     np.testing.assert_array_equal(_u8(layer.qbuf[:n]), ref["qbuf"][:n])
-    np.testing.assert_array_equal(_u8(layer.sbuf[:n]), ref["sbuf"][:n])
+    np.testing.assert_array_equal(_u8s(layer.sbuf[:n], cfg.d), ref["sbuf"][:n])
     if n > 0:
-        _check_h(_u8(layer.h_q[:n]), _u8(layer.h_s[:n]), ref["h_q"][:n], ref["h_s"][:n], "h")
+        _check_h(_u8(layer.h_q[:n]), _u8s(layer.h_s[:n], cfg.F), ref["h_q"][:n], ref["h_s"][:n],
+                 "h")
         _check_e2e(to_np(layer.y[:n]), ref["y"][:n], "y")
     assert bool(is_poison(layer.y[n:]).all())
     _check_e2e(to_np(layer.out), ref["out"], "out")
 
 
-@pytest.mark.parametrize("name", ["olmoe_bf16", "zipf_skew_bf16", "finegrained_shard_bf16",
-                                  "zipf_dropless_bf16"])
+@pytest.mark.parametrize("name", ["olmoe_bf16", "gptoss_shard_bf16", "zipf_skew_bf16",
+                                  "finegrained_shard_bf16", "zipf_dropless_bf16"])
 def test_full_config_mx(name):
     """Full workload sizes: MoELayer.forward_mx; routing and quantize-on-dispatch
     checked bit-exactly (the whole route map, 256+ sampled dispatch rows),
@@ -253,33 +286,35 @@ def test_full_config_mx(name):
     eq, es = orc.mx_quantize(x[src])
     sel = torch.from_numpy(rows).cuda()
     np.testing.assert_array_equal(_u8(layer.qbuf[sel]), eq)
-    np.testing.assert_array_equal(_u8(layer.sbuf[sel]), es)
+    np.testing.assert_array_equal(_u8s(layer.sbuf[sel], d), es)
     # expert outputs on sampled rows of sampled experts (the GPU's quantized
     # weights of those experts checked bit-exactly first, then used by the oracle)
     nonempty = [j for j in range(E_L) if off[j + 1] > off[j]]
     experts = sorted({nonempty[0], nonempty[-1], int(rng.choice(nonempty))})
-    wcache = {}
 
     def wq(j):
-        if j not in wcache:
+        # the oracle's quantized weights of expert j, kept for the session:
+        # workloads drawn from the same seed and shapes share them
+        key = (cfg.seed, cfg.N, cfg.d, cfg.F, cfg.ep_size, cfg.ep_rank, j)
+        if key not in _WQ_CACHE:
             gq, gs = orc.mx_quantize(_f64(inp.w_gu[j]))
             dq, ds = orc.mx_quantize(_f64(inp.w_d[j]))
-            wcache[j] = (gq, gs, dq, ds)
-        return wcache[j]
+            _WQ_CACHE[key] = (gq, gs, dq, ds)
+        return _WQ_CACHE[key]
 
     for j in experts:
         gq, gs, dq, ds = wq(j)
         np.testing.assert_array_equal(_u8(mxw.w_gu_q[j]), gq)
-        np.testing.assert_array_equal(_u8(mxw.w_d_s[j]), ds)
+        np.testing.assert_array_equal(_u8s(mxw.w_d_s[j], F), ds)
         a, b = int(off[j]), int(off[j + 1])
         Xq, Xs = orc.mx_quantize(x[ref["row_src"][a:b] // K])
         Hq, Hs, Y = orc.expert_ffn_mx_rows(Xq, Xs, gq, gs, dq, ds)
-        _check_h(_u8(layer.h_q[a:b]), _u8(layer.h_s[a:b]), Hq, Hs, f"h expert {j}")
+        _check_h(_u8(layer.h_q[a:b]), _u8s(layer.h_s[a:b], F), Hq, Hs, f"h expert {j}")
         _check_e2e(to_np(layer.y[a:b]), Y, f"y expert {j}")
     # combined output of 512 whole tokens: each kept local route's expert row
     # recomputed by the oracle (grouped by expert), then the oracle's combine
     toks = np.unique(np.concatenate([[0, cfg.T - 1],
-                                     rng.choice(cfg.T, size=MX_TOKENS - 2, replace=False)]))
+                                     1 + rng.choice(cfg.T - 2, size=MX_TOKENS - 2, replace=False)]))
     assert len(toks) == MX_TOKENS
     dr, drow = ref["dest_rank"][toks], ref["dest_row"][toks]
     rows = np.unique(drow[(dr == cfg.ep_rank) & (drow >= 0)])
@@ -287,10 +322,8 @@ def test_full_config_mx(name):
     y_rows = {}
     for j in np.unique(expert_of):
         rj = rows[expert_of == j]
-        gq, gs = orc.mx_quantize(_f64(inp.w_gu[int(j)]))
-        dq, ds = orc.mx_quantize(_f64(inp.w_d[int(j)]))
         Xq, Xs = orc.mx_quantize(x[ref["row_src"][rj] // K])
-        y_rows.update(zip(rj.tolist(), orc.expert_ffn_mx_rows(Xq, Xs, gq, gs, dq, ds)[2]))
+        y_rows.update(zip(rj.tolist(), orc.expert_ffn_mx_rows(Xq, Xs, *wq(int(j)))[2]))
     expect = orc.combine_tokens(toks, lambda r: y_rows[r], ref["dest_rank"], ref["dest_row"],
                                 ref["topk_w"], cfg.ep_rank, d, "bf16")
     _check_e2e(to_np(layer.out[torch.from_numpy(toks).cuda()]), expect, "out")
@@ -301,6 +334,9 @@ def test_mx_calls_reject_what_they_do_not_cover():
     import ctypes
     f32 = moe.MoeShape.from_config(MX_SMALL[0].with_(dtype="f32")).c()
     assert lib.moe_dispatch_rows_mx(ctypes.byref(f32), 16, 16, 16, 16, 16, None) == _abi.MOE_EDTYPE
-    odd = moe.MoeShape.from_config(CONFIGS["gptoss_shard_bf16"]).c()   # d = 2880
+    # d = 2848 = 32 * 89: not a whole number of 64-element MFMA K slices
+    odd = moe.MoeShape.from_config(CONFIGS["gptoss_shard_bf16"].with_(d=2848)).c()
     assert lib.moe_expert_up_mx(ctypes.byref(odd), *([16] * 7), None) == _abi.MOE_EINVAL
+    odd_f = moe.MoeShape.from_config(CONFIGS["gptoss_shard_bf16"].with_(F=3040)).c()
+    assert lib.moe_expert_down_mx(ctypes.byref(odd_f), *([16] * 6), None) == _abi.MOE_EINVAL
     assert lib.moe_mx_quantize_rows(4, 48, 16, 16, 16, None) == _abi.MOE_EINVAL

@@ -30,7 +30,9 @@ import pytest
 import combine_top_softmax_amd.build as B
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["ffn.hip", "bwd.hip", "mx.hip"]
+SOURCES = ["ffn.hip", "bwd.hip", "mx.hip", "route.hip", "rows.hip"]
+# sources whose kernels issue the hand-written direct loads
+DMA_SOURCES = ["ffn.hip", "bwd.hip", "mx.hip"]
 
 _SREG = re.compile(r"^s\[(\d+):(\d+)\]$|^s(\d+)$|^(m0|vcc|vcc_lo|vcc_hi|exec)$")
 
@@ -123,7 +125,7 @@ def listings():
             return dict(zip(SOURCES, ex.map(lambda s: _compile(s, d), SOURCES)))
 
 
-@pytest.mark.parametrize("src", SOURCES)
+@pytest.mark.parametrize("src", DMA_SOURCES)
 def test_direct_loads_respect_wait_states(listings, src):
     n, bad = direct_load_hazards(listings[src])
     assert n > 0, f"{src}: no direct loads found (listing format changed?)"
@@ -152,3 +154,24 @@ def test_checker_flags_a_valu_written_base():
     # writer hidden behind a label
     assert len(direct_load_hazards("s_mov_b32 m0, s2\n.LBB0_1:\ns_nop 0\n"
                                    "global_load_lds_dwordx4 v[2:3], off")[1]) == 1
+
+
+def kernel_resources(asm: str) -> dict:
+    """Per kernel of a listing's metadata: (private segment bytes, VGPR spills)."""
+    names = re.findall(r"^\s+\.name:\s+(\S+)", asm, flags=re.M)
+    priv = re.findall(r"^\s+\.private_segment_fixed_size:\s+(\d+)", asm, flags=re.M)
+    spill = re.findall(r"^\s+\.vgpr_spill_count:\s+(\d+)", asm, flags=re.M)
+    assert len(names) == len(priv) == len(spill) and names, "kernel metadata not found"
+    return {n: (int(p), int(v)) for n, p, v in zip(names, priv, spill)}
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_kernel_spills_to_scratch(listings, src):
+    """No kernel keeps registers in scratch memory. The GEMMs' hand-written
+    waits count only their own direct loads; compiler-made scratch loads and
+    stores would be vector-memory traffic outside that bookkeeping (and a
+    spilled main loop is slow): a kernel that needs more registers than a
+    wave has must be restructured, not left to spill."""
+    res = kernel_resources(listings[src])
+    bad = {k: v for k, v in res.items() if v != (0, 0)}
+    assert not bad, f"{src}: kernels with scratch use (bytes, VGPR spills): {bad}"
