@@ -21,7 +21,7 @@ from ._abi import MoeError  # noqa: F401
 
 __all__ = [
     "MoeShape", "RouteOut", "MoELayer", "MoeError", "moe_route_workspace_size", "moe_route",
-    "moe_route_map", "moe_dispatch_rows", "moe_expert_ffn", "moe_expert_up",
+    "moe_route_map", "moe_route_noalloc", "moe_dispatch_rows", "moe_expert_ffn", "moe_expert_up",
     "moe_expert_down", "moe_combine", "moe_combine_bwd", "moe_expert_ffn_bwd",
     "moe_expert_ffn_bwd_data", "moe_expert_ffn_bwd_weight", "moe_expert_up_save_gu",
     "moe_expert_ffn_bwd_data_saved_gu",
@@ -167,6 +167,17 @@ def moe_route(shape: MoeShape, logits: torch.Tensor, out: RouteOut, ws: torch.Te
     rc = _abi.load().moe_route(ctypes.byref(shape.c()), _ptr(logits), ctypes.byref(out.c()),
                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _abi.check("moe_route", rc)
+
+
+def moe_route_noalloc(shape: MoeShape, logits: torch.Tensor, out: RouteOut,
+                      stream=None) -> None:
+    """moe_route on the library's static per-GPU scratch: no workspace, no
+    allocation (see include/moe.h for its size limit and sharing rules)."""
+    _need(logits, "logits", (shape.T, shape.N), torch.float32)
+    out.check(shape)
+    rc = _abi.load().moe_route_noalloc(ctypes.byref(shape.c()), _ptr(logits),
+                                       ctypes.byref(out.c()), _stream(stream))
+    _abi.check("moe_route_noalloc", rc)
 
 
 def moe_route_map(shape: MoeShape, topk_idx_in: torch.Tensor, out: RouteOut, ws: torch.Tensor,

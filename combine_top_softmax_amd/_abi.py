@@ -12,6 +12,8 @@ MOE_EDTYPE = -2
 MOE_EALIGN = -3
 MOE_EWORKSPACE = -4
 MOE_EHIP = -5
+MOE_ESCRATCH = -6
+MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
 MOE_MAX_K = 16
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_WIDTH = 1 << 20
@@ -40,6 +42,7 @@ SIGNATURES = {
     "moe_route_workspace_size": (ctypes.c_int, [_SHAPE, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_route": (ctypes.c_int, [_SHAPE, _P, _ROUTE, _P, ctypes.c_size_t, _P]),
     "moe_route_map": (ctypes.c_int, [_SHAPE, _P, _ROUTE, _P, ctypes.c_size_t, _P]),
+    "moe_route_noalloc": (ctypes.c_int, [_SHAPE, _P, _ROUTE, _P]),
     "moe_dispatch_rows": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_expert_ffn": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P, _P]),
     "moe_buffer_rows": (ctypes.c_int64, [_SHAPE]),

@@ -6,6 +6,14 @@
 // metadata, capacity-shaped buffers fixed before the loop).
 #include "moe_internal.h"
 
+#include <mutex>
+
+// Workspace of moe_route_noalloc: one static array per GPU, alive until the
+// process ends. Host code never uses the symbol itself as an address (on the
+// host it only names the array); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using moe::ceil_div;
@@ -60,6 +68,28 @@ int check_route_out(const moe_shape_t &s, const moe_route_out_t *o, bool need_to
   return MOE_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices] = {};
+
+int scratch_address(void **addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();   // do not leave the error for the next launch check
+      return MOE_EHIP;
+    }
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,6 +109,9 @@ const char *moe_strerror(int code) {
     case MOE_EALIGN: return "data pointer is NULL or misaligned (16 bytes for rows, 4 for int32/fp32 arrays)";
     case MOE_EWORKSPACE: return "workspace is NULL or smaller than moe_route_workspace_size";
     case MOE_EHIP: return "HIP kernel launch failed";
+    case MOE_ESCRATCH:
+      return "the shape's route workspace exceeds the static no-allocation scratch "
+             "(MOE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error code";
   }
 }
@@ -98,6 +131,19 @@ int moe_route(const moe_shape_t *shape, const float *logits, const moe_route_out
   if (shape->T > 0 && !aligned16(logits)) return MOE_EALIGN;
   if ((rc = check_route_out(*shape, out, true)) != MOE_OK) return rc;
   if (!aligned4(ws) || ws_bytes < route_ws_bytes(*shape)) return MOE_EWORKSPACE;
+  return moe::launch_route(*shape, logits, nullptr, *out, ws, stream);
+}
+
+int moe_route_noalloc(const moe_shape_t *shape, const float *logits, const moe_route_out_t *out,
+                      hipStream_t stream) {
+  int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (shape->T > 0 && !aligned16(logits)) return MOE_EALIGN;
+  if ((rc = check_route_out(*shape, out, true)) != MOE_OK) return rc;
+  const size_t need = route_ws_bytes(*shape);
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ESCRATCH;
+  void *ws = nullptr;
+  if ((rc = scratch_address(&ws)) != MOE_OK) return rc;
   return moe::launch_route(*shape, logits, nullptr, *out, ws, stream);
 }
 

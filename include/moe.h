@@ -54,6 +54,7 @@ typedef struct ihipStream_t *hipStream_t;
 #define MOE_EALIGN     -3  /* a data pointer is NULL or not 16-byte aligned         */
 #define MOE_EWORKSPACE -4  /* workspace NULL or smaller than moe_route_workspace_size */
 #define MOE_EHIP       -5  /* the HIP runtime rejected a kernel launch              */
+#define MOE_ESCRATCH   -6  /* the shape needs more than MOE_NOALLOC_SCRATCH_BYTES   */
 
 /* Limits of this implementation (MOE_EINVAL beyond them). */
 #define MOE_MAX_K        16     /* top-K                     */
@@ -141,6 +142,26 @@ int moe_route_workspace_size(const moe_shape_t *shape, size_t *bytes);
  * contents on entry do not matter). */
 int moe_route(const moe_shape_t *shape, const float *logits, const moe_route_out_t *out,
               void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_route without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES held by the library on every GPU it runs on until
+ * the process ends; the call allocates nothing and frees nothing. Outputs,
+ * validation and kernels are those of moe_route, and the results are equal
+ * bit for bit. The first call on a device (with that device current) looks
+ * up the array's address with hipGetSymbolAddress, so make one call outside
+ * a graph capture before capturing. Returns MOE_ESCRATCH when
+ * moe_route_workspace_size(shape) exceeds MOE_NOALLOC_SCRATCH_BYTES (the
+ * workspace is 4*N/64 + K bytes per token: with N = 256 and K = 8 up to about
+ * 699,000 tokens fit), MOE_EHIP when
+ * the address lookup fails. Every call on one GPU shares the array: calls
+ * that may run concurrently on one GPU (different streams without ordering,
+ * or different host threads) race and give undefined results; calls ordered
+ * on one stream do not. Nothing in the array has to start at zero. */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int moe_route_noalloc(const moe_shape_t *shape, const float *logits, const moe_route_out_t *out,
+                      hipStream_t stream);
 
 /* The route-map builder alone (Olmo-core MoE report Sec. 5.4): as moe_route
  * but from given ids. topk_idx_in [T,K] int32, -1 = invalid route (gets
