@@ -51,10 +51,17 @@ def parse():
     return p.parse_args()
 
 
+def code_sha256(path: str) -> str:
+    """sha256 of a source file's code: `//` comments, trailing blanks and empty
+    lines removed, so that an edit of the comments alone keeps the key."""
+    import hashlib
+    lines = (ln.split("//", 1)[0].rstrip() for ln in open(path).read().splitlines())
+    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()
+
+
 def traffic_from_profile(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from profiles/<workload>_gemm_<kernel>_traffic.md,
-    or None when the file is missing or the kernel source changed since it was taken."""
-    import hashlib
+    or None when the file is missing or the kernel's code changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"{workload}_gemm_{kernel}_traffic.md")
     if not os.path.exists(path):
         return None
@@ -65,7 +72,7 @@ def traffic_from_profile(workload: str, kernel: str):
             kv[k.strip()] = v.strip()
     try:
         src = os.path.join(ROOT, kv["source"])
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["source_sha256"]:
+        if code_sha256(src) != kv["source_code_sha256"]:
             return None
         return (float(kv["fetch_kib_per_launch"]) * float(kv["fetch_factor"]) +
                 float(kv["write_kib_per_launch"]) * float(kv["write_factor"])) * 1024.0

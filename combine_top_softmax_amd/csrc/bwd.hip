@@ -120,7 +120,8 @@ __global__ __launch_bounds__(256) void k_combine_bwd(
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c = seg + i * 64 + lane;
-      g[i] = (FULL || c < nvec) ? dout[(size_t)t * nvec + c] : u32x4_t{0, 0, 0, 0};
+      g[i] = (FULL || c < nvec) ? __builtin_nontemporal_load(dout + (size_t)t * nvec + c)
+                                : u32x4_t{0, 0, 0, 0};
     }
     for (uint64_t rest = local; rest != 0;) {
       const int ka = __builtin_ctzll(rest);
@@ -134,9 +135,9 @@ __global__ __launch_bounds__(256) void k_combine_bwd(
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int c = seg + i * 64 + lane;
-        if (FULL || c < nvec) {
-          ya[i] = y[ra * nvec + c];
-          if (hb) yb[i] = y[rb * nvec + c];
+        if (FULL || c < nvec) {   // read once: nontemporal (as the forward combine)
+          ya[i] = __builtin_nontemporal_load(y + ra * nvec + c);
+          if (hb) yb[i] = __builtin_nontemporal_load(y + rb * nvec + c);
         }
       }
       const float da = wave_sum(route(g, ya, ra, __builtin_bit_cast(float,

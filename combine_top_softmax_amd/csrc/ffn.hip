@@ -26,10 +26,10 @@
 // that XCD's L2.
 //
 // bf16 paths (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
-//   k_gemm_bf16_big (K % 64 == 0): 256 x 256 block tile, 8 waves of 128 x 64
-//     (two per SIMD), operands loaded global -> LDS directly,
-//     XOR-swizzled LDS rows, two LDS stages, loads and fragment reads
-//     interleaved with the MFMAs (details at the kernel);
+//   k_gemm_bf16_big (K % 64 == 0): 256 x 256 block tile, 4 waves of 128 x 128
+//     (one per SIMD), operands loaded global -> LDS directly,
+//     XOR-swizzled LDS rows, two A and three weight LDS stages, loads and
+//     fragment reads interleaved with the MFMAs (details at the kernel);
 //   k_gemm_bf16 (any K % 8 == 0): 128 x 128 block tile, 4 waves of 64 x 64,
 //     register-staged LDS double buffer with 16-byte row padding.
 // fp32 path: a plain LDS-tiled SIMT kernel (64 x 64 tile, 4 x 4 per thread).
