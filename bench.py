@@ -10,8 +10,9 @@ overflow and the drop path runs).
 Prints one JSON line. ``value`` is routed token-rows per second (kept routes
 to this GPU's experts per layer forward / mean layer time over the timed
 steps). Stage times come from HIP events recorded between the calls on the
-stream the kernels run on; the per-step median and spread are reported beside
-the mean.
+stream the kernels run on, created for timing only (no system-scope cache
+fence at each record); the per-step median and spread are reported beside the
+mean.
 """
 from __future__ import annotations
 
@@ -149,7 +150,7 @@ def time_mx(args, layer, inp, stream, torch) -> dict:
     for _ in range(args.warmup):
         mstep()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.set_sync_debug_mode("error")
     for i in range(args.steps):
         mstep(evs[i])
@@ -217,7 +218,7 @@ def time_backward(args, layer, inp, stream, torch) -> dict:
         for _ in range(args.warmup):
             bstep(saved=saved)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        evs = [[TimingEvent() for _ in range(6)]
                for _ in range(args.steps)]
         torch.cuda.set_sync_debug_mode("error")
         for i in range(args.steps):
@@ -235,7 +236,7 @@ def time_backward(args, layer, inp, stream, torch) -> dict:
              (lambda: moe.moe_expert_up(s, layer.buf, r.offsets, inp.w_gu, layer.h))
         for _ in range(args.warmup):
             fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         e0.record(stream)
         for _ in range(args.steps):
             fn()
@@ -264,6 +265,59 @@ def time_backward(args, layer, inp, stream, torch) -> dict:
                          "expert_up_ms": round(up_ms, 5),
                          "expert_up_save_gu_ms": round(up_save_ms, 5),
                          "train_step_saving_ms": round(ms - ms_saved - (up_save_ms - up_ms), 5)}}
+
+
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence.
+
+    torch.cuda.Event records with a system-scope release: each record writes
+    back and invalidates the caches of all eight XCDs, which adds a few
+    microseconds to the stage it closes and slows the one it opens. HIP offers
+    this flag for events used only to measure time; the timestamps are the
+    same end-of-pipe ones. Elapsed times are read after a device
+    synchronization. Same interface as torch.cuda.Event: record(stream),
+    elapsed_time(other) in ms."""
+    _hip = None
+    _DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            # torch has loaded the HIP runtime; bind to that instance only
+            lib = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | ctypes.RTLD_GLOBAL)
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                    ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        rc = self._lib().hipEventCreateWithFlags(ctypes.byref(self.h), self._DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = self._lib().hipEventRecord(self.h, self._ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, other) -> float:
+        ms = self._ct.c_float()
+        rc = self._lib().hipEventElapsedTime(self._ct.byref(ms), self.h, other.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.h:
+            self._hip.hipEventDestroy(self.h)
 
 
 def _quantile(sorted_vals, q):
@@ -338,7 +392,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.set_sync_debug_mode("error")      # any host sync in the loop raises
     marker = _range_push("steady_state_forward_loop")   # named range for a HIP API trace
     t_host0 = time.perf_counter()
@@ -356,7 +410,7 @@ def main():
         step()
     graph.replay()
     torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0, g1 = TimingEvent(), TimingEvent()
     g0.record(stream)
     for _ in range(args.steps):
         graph.replay()
@@ -446,6 +500,7 @@ def main():
         "dispatch_combine_hbm_frac": round(dc_bytes / dc_t / 1e9 / HBM_PEAK_GBPS, 4),
         "gemm_TFLOPs": round(6.0 * R * d * F / ffn_t / 1e12, 1),
         "gemm_mfma_frac": round(6.0 * R * d * F / ffn_t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "timing": "HIP events on the kernels' stream, hipEventDisableSystemFence",
         "host_enqueue_ms_per_step": round(t_host * 1e3 / args.steps, 4),
         "graph_replay_ms_per_step": round(graph_ms, 5),
         "backward": backward,

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void k_combine_bwd(
     const u32x4_t *__restrict__ dout, const u32x4_t *__restrict__ y,
     const int32_t *__restrict__ dest_rank, const int32_t *__restrict__ dest_row,
     const float *__restrict__ w, u32x4_t *__restrict__ dy, float *__restrict__ dw, int T, int K,
-    int nvec, int ep_rank) {
+    int nvec, int ep_rank, int rows) {
   const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6));
   if (t >= T) return;
@@ -87,7 +87,8 @@ __global__ __launch_bounds__(256) void k_combine_bwd(
     m_row = dest_row[q0 + lane];
     m_w = w[q0 + lane];
   }
-  const uint64_t local = __ballot(m_rank == ep_rank);
+  // a local route whose row lies outside the buffer is skipped (dw = 0)
+  const uint64_t local = __ballot(m_rank == ep_rank && (unsigned)m_row < (unsigned)rows);
   float dw_mine = 0.f;   // lane k < K accumulates route k's weight gradient
   // dY row segment = w * dOut; returns this lane's part of <dOut, Y[row]>
   auto route = [&](const u32x4_t (&g)[NV], const u32x4_t (&yv)[NV], size_t row, float wk,
@@ -891,11 +892,12 @@ template <bool BF16, bool FULL>
 void combine_bwd_nv(int nv, dim3 grid, hipStream_t st, const u32x4_t *g, const u32x4_t *y,
                     const int32_t *dr, const int32_t *drow, const float *w, u32x4_t *o,
                     float *dw, const moe_shape_t &s, int nvec) {
+  const int rows = (int)buffer_rows(s);
   switch (nv) {
-    case 1: hipLaunchKernelGGL((k_combine_bwd<BF16, 1, FULL>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
-    case 2: hipLaunchKernelGGL((k_combine_bwd<BF16, 2, FULL>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
-    case 4: hipLaunchKernelGGL((k_combine_bwd<BF16, 4, FULL>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
-    default: hipLaunchKernelGGL((k_combine_bwd<BF16, 8, FULL>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank); break;
+    case 1: hipLaunchKernelGGL((k_combine_bwd<BF16, 1, FULL>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank, rows); break;
+    case 2: hipLaunchKernelGGL((k_combine_bwd<BF16, 2, FULL>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank, rows); break;
+    case 4: hipLaunchKernelGGL((k_combine_bwd<BF16, 4, FULL>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank, rows); break;
+    default: hipLaunchKernelGGL((k_combine_bwd<BF16, 8, FULL>), grid, dim3(256), 0, st, g, y, dr, drow, w, o, dw, s.T, s.K, nvec, s.ep_rank, rows); break;
   }
 }
 

@@ -98,7 +98,7 @@ template <bool ROUTED>
 __global__ __launch_bounds__(256) void k_quant_rows(
     const u32x4_t *__restrict__ x, const int32_t *__restrict__ dest_rank,
     const int32_t *__restrict__ dest_row, uint8_t *__restrict__ qdata,
-    uint8_t *__restrict__ scales, int64_t n_src, int K, int d, int ep_rank) {
+    uint8_t *__restrict__ scales, int64_t n_src, int K, int d, int ep_rank, int64_t rows) {
   const int lane = threadIdx.x & 63;
   const int64_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= n_src) return;
@@ -119,8 +119,8 @@ __global__ __launch_bounds__(256) void k_quant_rows(
     if constexpr (ROUTED) {
       for (int k = 0; k < K; ++k) {
         const int64_t qk = t * K + k;
-        if (dest_rank[qk] != ep_rank) continue;
         const int64_t row = dest_row[qk];
+        if (dest_rank[qk] != ep_rank || row < 0 || row >= rows) continue;   // outside: skipped
         *reinterpret_cast<u32x2_t *>(qdata + row * d + (int64_t)c * 8) = q;
         if ((c & 3) == 0) scales[row * nblk + (c >> 2)] = sc;
       }
@@ -511,7 +511,7 @@ int launch_quantize_rows(int64_t rows, int cols, const void *src, uint8_t *qdata
                          hipStream_t st) {
   hipLaunchKernelGGL(k_quant_rows<false>, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, st,
                      static_cast<const u32x4_t *>(src), nullptr, nullptr, qdata, scales, rows, 1,
-                     cols, 0);
+                     cols, 0, rows);
   return launch_status();
 }
 
@@ -519,7 +519,7 @@ int launch_dispatch_mx(const moe_shape_t &s, const void *x, const int32_t *dest_
                        const int32_t *dest_row, uint8_t *qbuf, uint8_t *sbuf, hipStream_t st) {
   hipLaunchKernelGGL(k_quant_rows<true>, dim3((unsigned)ceil_div(s.T, 4)), dim3(256), 0, st,
                      static_cast<const u32x4_t *>(x), dest_rank, dest_row, qbuf, sbuf,
-                     (int64_t)s.T, s.K, s.d, s.ep_rank);
+                     (int64_t)s.T, s.K, s.d, s.ep_rank, buffer_rows(s));
   return launch_status();
 }
 

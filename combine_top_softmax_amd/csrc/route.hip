@@ -23,6 +23,9 @@
 //   k_assign       one wave per tile: every block rebuilds the exclusive scan
 //                  of min(counts, C) over experts in LDS, then p = base + rank,
 //                  keep iff p < C, row = offset of e on its rank + p.
+// Small route maps (N <= 256, <= 256 tiles, N * tiles <= 16384) take two kernels:
+// k_assign_scan does the work of the last two, each block summing the
+// histogram columns itself.
 //
 // Workspace: hist/base [N][ntiles] int32, then rank [T*K] uint8.
 #include "moe_internal.h"
@@ -388,6 +391,129 @@ __global__ __launch_bounds__(64) void k_assign(
   }
 }
 
+// k_assign with the tile scan folded in, for small route maps (N <= 256, at
+// most 256 tiles and N * ntiles <= kFusedScanMax, i.e. at most 64 KiB of histogram per
+// block and 16 MiB of L2 reads in all): every block reads the whole histogram
+// and forms its own tile's bases and the expert totals, which saves the
+// k_tile_scan launch and its round trip. The histogram is only read,
+// so the blocks do not race. 4 waves: G = 256 / N (a power of two, <= 64)
+// threads per expert sum interleaved tiles; partial sums meet in LDS; wave 0
+// scans min(count, C) over the experts; then lane = token, wave w writes the
+// slots k with k % 4 == w.
+constexpr int kFusedScanMax = 16384;
+
+template <int KM>
+__global__ __launch_bounds__(256) void k_assign_scan(
+    const int32_t *__restrict__ ids, const int32_t *__restrict__ hist,
+    const uint8_t *__restrict__ rank_ws, int32_t *__restrict__ counts,
+    int32_t *__restrict__ dest_rank, int32_t *__restrict__ dest_row,
+    uint8_t *__restrict__ drop_mask, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ row_src, int T, int N, int K, int C, int E_L, int ep_size,
+    int ep_rank, int ntiles, int rows, int G) {
+  __shared__ int s_below[256], s_tot[256];     // partial sums, one per thread
+  __shared__ int s_base[MOE_MAX_EXPERTS];     // routes to e in the tiles before this one
+  __shared__ int s_g[MOE_MAX_EXPERTS + 1];    // exclusive scan of min(counts, C)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = blockIdx.x;
+  const int t = tile * kRouteTile + lane;
+  // this token's experts and in-tile ranks, loaded ahead of the scan
+  int e[KM];
+  uint8_t rk[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    e[k] = -1;
+    rk[k] = 0;
+    if (k < K && (k & 3) == wv && t < T) {
+      e[k] = ids[(size_t)t * K + k];
+      rk[k] = rank_ws[(size_t)t * K + k];
+    }
+  }
+  {
+    // thread (expert ex, part q) sums tiles q, q + G, ... of column ex
+    const int ex = tid / G, q = tid - ex * G;
+    int below = 0, tot = 0;
+    if (ex < N) {
+      const int32_t *col = hist + (size_t)ex * ntiles;
+#pragma unroll 8
+      for (int tt = q; tt < ntiles; tt += G) {
+        const int v = col[tt];
+        tot += v;
+        below += tt < tile ? v : 0;
+      }
+    }
+    s_below[tid] = below;
+    s_tot[tid] = tot;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    // per lane a run of experts: totals from the partial sums, then the scan
+    const int per = (N + kWave - 1) / kWave;
+    const int beg = lane * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i) {
+      const int ex = beg + i;
+      if (ex < N) {
+        int b = 0, c = 0;
+        for (int j = 0; j < G; ++j) {
+          b += s_below[ex * G + j];
+          c += s_tot[ex * G + j];
+        }
+        s_base[ex] = b;
+        s_tot[ex * G] = c;           // the expert's total, in its first slot
+        if (tile == 0) counts[ex] = c;
+        local += min(c, C);
+      }
+    }
+    const int incl = wave_incl_scan_dpp(local);
+    int run = incl - local;
+    for (int i = 0; i < per; ++i) {
+      const int ex = beg + i;
+      if (ex < N) {
+        s_g[ex] = run;
+        run += min(s_tot[ex * G], C);
+      }
+    }
+    if (lane == 63) s_g[N] = incl;
+  }
+  __syncthreads();
+  if (tile == 0) {
+    const int n_off = ep_size * (E_L + 1);
+    for (int i = tid; i < n_off; i += 256) {
+      const int r = i / (E_L + 1), j = i % (E_L + 1);
+      offsets[i] = s_g[r * E_L + j] - s_g[r * E_L];
+    }
+  }
+  if (t < T) {
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (k >= K || (k & 3) != wv) continue;
+      const size_t qi = (size_t)t * K + k;
+      const int p = (e[k] >= 0 && e[k] < N) ? s_base[e[k]] + (int)rk[k] : -1;
+      int drk = -1, drw = -1;
+      uint8_t drop = 0;
+      if (p >= 0) {
+        if (p < C) {
+          const int r = e[k] / E_L;
+          drk = r;
+          drw = s_g[e[k]] - s_g[r * E_L] + p;
+          if (row_src != nullptr && r == ep_rank) row_src[drw] = (int32_t)qi;
+        } else {
+          drop = 1;
+        }
+      }
+      dest_rank[qi] = drk;
+      dest_row[qi] = drw;
+      drop_mask[qi] = drop;
+    }
+  }
+  if (row_src != nullptr) {
+    const int used = s_g[(ep_rank + 1) * E_L] - s_g[ep_rank * E_L];
+    for (int64_t r = used + (int64_t)tile * 256 + tid; r < rows; r += (int64_t)ntiles * 256)
+      row_src[r] = -1;
+  }
+}
+
 template <int KM>
 int launch_route_km(const moe_shape_t &s, const float *logits, const int32_t *ids_in,
                     const moe_route_out_t &o, int32_t *hist, uint8_t *rank_ws, int ntiles,
@@ -400,10 +526,21 @@ int launch_route_km(const moe_shape_t &s, const float *logits, const int32_t *id
     hipLaunchKernelGGL((k_route_tile<KM, false>), dim3(ntiles), dim3(64 * kRouteWaves), 0, st,
                        nullptr, ids_in, nullptr, nullptr, hist, rank_ws, s.T, s.N, s.K, ntiles);
   if (launch_status() != MOE_OK) return MOE_EHIP;
-  hipLaunchKernelGGL(k_tile_scan, dim3(s.N), dim3(256), 0, st, hist, o.counts, ntiles);
-  if (launch_status() != MOE_OK) return MOE_EHIP;
   const int32_t *ids = logits != nullptr ? o.topk_idx : ids_in;
   const int E_L = s.N / s.ep_size;
+  if (s.N <= 256 && ntiles <= 256 && s.N * ntiles <= kFusedScanMax) {
+    // threads per expert: the largest power of two <= min(64, 256 / N), so that
+    // the N * G partial sums fit the block's 256 threads
+    int G = 1;
+    while (G < 64 && 2 * G * s.N <= 256) G *= 2;
+    hipLaunchKernelGGL((k_assign_scan<KM>), dim3(ntiles), dim3(256), 0, st, ids, hist, rank_ws,
+                       o.counts, o.dest_rank, o.dest_row, o.drop_mask, o.offsets, o.row_src,
+                       s.T, s.N, s.K, s.capacity, E_L, s.ep_size, s.ep_rank, ntiles,
+                       (int)buffer_rows(s), G);
+    return launch_status();
+  }
+  hipLaunchKernelGGL(k_tile_scan, dim3(s.N), dim3(256), 0, st, hist, o.counts, ntiles);
+  if (launch_status() != MOE_OK) return MOE_EHIP;
   hipLaunchKernelGGL((k_assign<KM>), dim3(ntiles), dim3(64), 0, st, ids, hist, rank_ws, o.counts,
                      o.dest_rank, o.dest_row, o.drop_mask, o.offsets, o.row_src, s.T, s.N,
                      s.K, s.capacity, E_L, s.ep_size, s.ep_rank, ntiles, (int)buffer_rows(s));

@@ -30,7 +30,7 @@ template <int NV, bool FULL>
 __global__ __launch_bounds__(256) void k_dispatch(
     const u32x4_t *__restrict__ x, const int32_t *__restrict__ dest_rank,
     const int32_t *__restrict__ dest_row, u32x4_t *__restrict__ buf, int T, int K,
-    int nvec, int ep_rank) {
+    int nvec, int ep_rank, int rows) {
   const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6));
   if (t >= T) return;
@@ -40,7 +40,8 @@ __global__ __launch_bounds__(256) void k_dispatch(
     m_rank = dest_rank[q0 + lane];
     m_row = dest_row[q0 + lane];
   }
-  const uint64_t local = __ballot(m_rank == ep_rank);
+  // a local route whose row lies outside the buffer is skipped
+  const uint64_t local = __ballot(m_rank == ep_rank && (unsigned)m_row < (unsigned)rows);
   if (local == 0) return;
   const u32x4_t *src = x + (size_t)t * nvec;
   for (int seg = 0; seg < nvec; seg += 64 * NV) {
@@ -72,7 +73,7 @@ template <bool BF16, int NV, bool FULL>
 __global__ __launch_bounds__(256) void k_combine(
     const u32x4_t *__restrict__ y, const int32_t *__restrict__ dest_rank,
     const int32_t *__restrict__ dest_row, const float *__restrict__ w,
-    u32x4_t *__restrict__ out, int T, int K, int nvec, int ep_rank) {
+    u32x4_t *__restrict__ out, int T, int K, int nvec, int ep_rank, int rows) {
   constexpr int EPV = BF16 ? 8 : 4;  // elements per 16-byte vector
   const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6));
@@ -85,7 +86,8 @@ __global__ __launch_bounds__(256) void k_combine(
     m_row = dest_row[q0 + lane];
     if (w != nullptr) m_w = w[q0 + lane];
   }
-  const uint64_t local = __ballot(m_rank == ep_rank);
+  // a local route whose row lies outside the buffer gathers nothing
+  const uint64_t local = __ballot(m_rank == ep_rank && (unsigned)m_row < (unsigned)rows);
   auto accumulate = [&](float (&acc)[NV][EPV], const u32x4_t (&v)[NV], float wk) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -167,23 +169,24 @@ inline int pick_nv(int nvec) {
 int launch_dispatch(const moe_shape_t &s, const void *x, const int32_t *dest_rank,
                     const int32_t *dest_row, void *buf, hipStream_t st) {
   const int nvec = s.d * elem_bytes(s.dtype) / 16;
+  const int rows = (int)buffer_rows(s);
   const dim3 grid((unsigned)ceil_div(s.T, kRowsPerBlock)), block(256);
   const u32x4_t *xv = static_cast<const u32x4_t *>(x);
   u32x4_t *bv = static_cast<u32x4_t *>(buf);
   const int nv = pick_nv(nvec);
   if (nvec % (64 * nv) == 0) {
     switch (nv) {
-      case 1: hipLaunchKernelGGL((k_dispatch<1, true>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank); break;
-      case 2: hipLaunchKernelGGL((k_dispatch<2, true>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank); break;
-      case 4: hipLaunchKernelGGL((k_dispatch<4, true>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank); break;
-      default: hipLaunchKernelGGL((k_dispatch<8, true>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank); break;
+      case 1: hipLaunchKernelGGL((k_dispatch<1, true>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank, rows); break;
+      case 2: hipLaunchKernelGGL((k_dispatch<2, true>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank, rows); break;
+      case 4: hipLaunchKernelGGL((k_dispatch<4, true>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank, rows); break;
+      default: hipLaunchKernelGGL((k_dispatch<8, true>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank, rows); break;
     }
   } else {
     switch (nv) {
-      case 1: hipLaunchKernelGGL((k_dispatch<1, false>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank); break;
-      case 2: hipLaunchKernelGGL((k_dispatch<2, false>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank); break;
-      case 4: hipLaunchKernelGGL((k_dispatch<4, false>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank); break;
-      default: hipLaunchKernelGGL((k_dispatch<8, false>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank); break;
+      case 1: hipLaunchKernelGGL((k_dispatch<1, false>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank, rows); break;
+      case 2: hipLaunchKernelGGL((k_dispatch<2, false>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank, rows); break;
+      case 4: hipLaunchKernelGGL((k_dispatch<4, false>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank, rows); break;
+      default: hipLaunchKernelGGL((k_dispatch<8, false>), grid, block, 0, st, xv, dest_rank, dest_row, bv, s.T, s.K, nvec, s.ep_rank, rows); break;
     }
   }
   return launch_status();
@@ -193,11 +196,12 @@ template <bool BF16, bool FULL>
 static void combine_nv(int nv, dim3 grid, hipStream_t st, const u32x4_t *y, const int32_t *dr,
                        const int32_t *drow, const float *w, u32x4_t *o, const moe_shape_t &s,
                        int nvec) {
+  const int rows = (int)buffer_rows(s);
   switch (nv) {
-    case 1: hipLaunchKernelGGL((k_combine<BF16, 1, FULL>), grid, dim3(256), 0, st, y, dr, drow, w, o, s.T, s.K, nvec, s.ep_rank); break;
-    case 2: hipLaunchKernelGGL((k_combine<BF16, 2, FULL>), grid, dim3(256), 0, st, y, dr, drow, w, o, s.T, s.K, nvec, s.ep_rank); break;
-    case 4: hipLaunchKernelGGL((k_combine<BF16, 4, FULL>), grid, dim3(256), 0, st, y, dr, drow, w, o, s.T, s.K, nvec, s.ep_rank); break;
-    default: hipLaunchKernelGGL((k_combine<BF16, 8, FULL>), grid, dim3(256), 0, st, y, dr, drow, w, o, s.T, s.K, nvec, s.ep_rank); break;
+    case 1: hipLaunchKernelGGL((k_combine<BF16, 1, FULL>), grid, dim3(256), 0, st, y, dr, drow, w, o, s.T, s.K, nvec, s.ep_rank, rows); break;
+    case 2: hipLaunchKernelGGL((k_combine<BF16, 2, FULL>), grid, dim3(256), 0, st, y, dr, drow, w, o, s.T, s.K, nvec, s.ep_rank, rows); break;
+    case 4: hipLaunchKernelGGL((k_combine<BF16, 4, FULL>), grid, dim3(256), 0, st, y, dr, drow, w, o, s.T, s.K, nvec, s.ep_rank, rows); break;
+    default: hipLaunchKernelGGL((k_combine<BF16, 8, FULL>), grid, dim3(256), 0, st, y, dr, drow, w, o, s.T, s.K, nvec, s.ep_rank, rows); break;
   }
 }
 

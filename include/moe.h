@@ -114,7 +114,13 @@ int64_t moe_buffer_rows(const moe_shape_t *shape);
  * Olmo-core MoE report Sec. 5.4: two [T,K] tensors give destination rank and
  * destination row, negative entries mark invalid or capacity-dropped routes;
  * the row is the expert's offset on its rank plus the number of earlier
- * accepted routes for that expert. */
+ * accepted routes for that expert.
+ * The row calls (moe_dispatch_rows, moe_combine, moe_combine_bwd,
+ * moe_dispatch_bwd, moe_dispatch_rows_mx) take route (t,k) as local when
+ * dest_rank[t,k] == ep_rank and 0 <= dest_row[t,k] < Rmax; a route of this
+ * rank whose row lies outside that range is skipped (nothing read or written
+ * for it, dw[t,k] = 0), so a route map from any source keeps them inside
+ * their buffers. moe_route and moe_route_map never produce such a route. */
 typedef struct {
   int32_t *topk_idx;
   float   *topk_w;

@@ -293,3 +293,89 @@ def test_row_buffers_past_2_32_elements():
     assert_rows_close(to_np(layer.y[sel]), np.array(Yq), 5e-2, "mx y past 2^32")
     del layer, inp, dout, dx
     torch.cuda.empty_cache()
+
+
+def test_row_calls_skip_rows_outside_the_buffer():
+    """A route map from elsewhere that gives routes of this rank rows outside
+    [0, Rmax): dispatch, combine, their backward and the MX dispatch skip those
+    routes (the documented semantics: as if not local) and touch no memory
+    outside their buffers. Each buffer is a view with two guard rows on either
+    side, so even an unchecked access would stay inside the allocation."""
+    cfg = LayerConfig("rows_outside", T=96, d=64, N=8, K=2, F=64, cf=Fraction(2), dtype="bf16",
+                      ep_size=2, ep_rank=1, seed=43)
+    shape = moe.MoeShape.from_config(cfg)
+    R, d, T, K, ep = shape.rows, cfg.d, cfg.T, cfg.K, cfg.ep_rank
+    inp = make_inputs(cfg, "cuda")
+    route = route_gpu(shape, inp.logits)
+    rank = route.dest_rank.clone()
+    row = route.dest_row.clone()
+    local = torch.nonzero(rank == ep)
+    assert local.shape[0] >= 8
+    for i, bad in enumerate((R, R + 1, -1, -2)):           # four local routes pushed outside
+        t, k = local[3 * i].tolist()
+        row[t, k] = bad
+    rank_np, row_np = to_np(rank), to_np(row)
+    outside = (rank_np == ep) & ((row_np < 0) | (row_np >= R))
+    assert int(outside.sum()) == 4
+    m_rank = np.where(outside, -1, rank_np)               # the oracle's view: not local
+    w = route.topk_w
+
+    def guarded(rows, cols, dtype, fill):
+        big = torch.empty(rows + 4, cols, dtype=dtype, device="cuda")
+        fill(big)
+        return big, big[2:2 + rows]
+
+    def guards_equal(big, ref):   # bit patterns (the poison is NaN)
+        b, r = big.view(torch.uint8), ref.view(torch.uint8)
+        return torch.equal(b[:2], r[:2]) and torch.equal(b[-2:], r[-2:])
+
+    # dispatch: guards untouched, kept rows = their token rows
+    big, buf = guarded(R, d, torch.bfloat16, poison_)
+    before = big.clone()
+    moe.moe_dispatch_rows(shape, inp.x, rank, row, buf)
+    torch.cuda.synchronize()
+    assert guards_equal(big, before)
+    ref = orc.dispatch_rows(to_np(inp.x), m_rank, row_np, ep, R)
+    wr = ~np.isnan(ref[:, 0])
+    np.testing.assert_array_equal(to_np(buf)[wr], ref[wr])
+
+    # combine and dispatch backward: data in the guard rows would show in the output
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    big_y = torch.randn(R + 4, d, generator=gen, device="cuda").to(torch.bfloat16)
+    y = big_y[2:2 + R]
+    out = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine(shape, y, rank, row, w, out)
+    dx = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    moe.moe_dispatch_bwd(shape, y, rank, row, dx)
+    torch.cuda.synchronize()
+    assert_rows_close(to_np(out), orc.combine(to_np(y), m_rank, row_np, to_np(w), ep, "bf16"),
+                      tol_of("bf16"), "combine")
+    assert_rows_close(to_np(dx), orc.dispatch_bwd(to_np(y), m_rank, row_np, ep, "bf16"),
+                      tol_of("bf16"), "dx")
+
+    # combine backward: guards of dy untouched, dw = 0 for the skipped routes
+    dout = torch.randn(T, d, generator=gen, device="cuda").to(torch.bfloat16)
+    big_dy, dy = guarded(R, d, torch.bfloat16, poison_)
+    before = big_dy.clone()
+    dw = torch.full((T, K), 7.0, device="cuda")
+    moe.moe_combine_bwd(shape, dout, y, rank, row, w, dy, dw)
+    torch.cuda.synchronize()
+    assert guards_equal(big_dy, before)
+    ref_dy, ref_dw = orc.combine_bwd(to_np(dout), to_np(y), m_rank, row_np, to_np(w), ep, R,
+                                     "bf16")
+    assert np.all(to_np(dw)[outside] == 0.0)
+    assert_rows_close(to_np(dw), ref_dw, tol_of("bf16"), "dw")
+    wr = ~np.isnan(ref_dy[:, 0])
+    assert_rows_close(to_np(dy)[wr], ref_dy[wr], tol_of("bf16"), "dy")
+
+    # MX dispatch: guards of both buffers untouched, kept rows bit-exact
+    sc = moe.mx_scale_cols(d)
+    big_q, qbuf = guarded(R, d, torch.uint8, lambda t: t.fill_(0xAB))
+    big_s, sbuf = guarded(R, sc, torch.uint8, lambda t: t.fill_(0xCD))
+    q_before, s_before = big_q.clone(), big_s.clone()
+    moe.moe_dispatch_rows_mx(shape, inp.x, rank, row, qbuf, sbuf)
+    torch.cuda.synchronize()
+    assert guards_equal(big_q, q_before) and guards_equal(big_s, s_before)
+    rq, rs, written = orc.dispatch_mx(to_np(inp.x), m_rank, row_np, ep, R)
+    np.testing.assert_array_equal(to_np(qbuf)[written], rq[written])
+    np.testing.assert_array_equal(to_np(sbuf)[written][:, :d // 32], rs[written])

@@ -157,8 +157,13 @@ def test_route_map_fig16_on_gpu(golden_dir):
         np.testing.assert_array_equal(to_np(out.drop_mask), ref["drop_mask"])
 
 
-@pytest.mark.parametrize("T,N,K,C,ep,frac", [(1000, 64, 8, 100, 4, 0.1), (65, 5, 5, 13, 5, 0.3),
-                                             (4097, 256, 6, 40, 8, 0.02), (1, 1, 1, 1, 1, 0.0)])
+@pytest.mark.parametrize("T,N,K,C,ep,frac", [
+    (1000, 64, 8, 100, 4, 0.1), (65, 5, 5, 13, 5, 0.3), (4097, 256, 6, 40, 8, 0.02),
+    (1, 1, 1, 1, 1, 0.0),
+    # both sides of each bound of the two-kernel route (N <= 256, <= 256 tiles,
+    # N * tiles <= 16384) and each group width of its column sums
+    (1000, 256, 8, 40, 4, 0.05), (4000, 257, 4, 30, 1, 0.0), (16384, 64, 2, 600, 2, 0.01),
+    (16385, 64, 2, 600, 2, 0.0), (300, 3, 2, 150, 1, 0.1), (5000, 100, 8, 300, 5, 0.02)])
 def test_route_map_random_ids_with_invalid(T, N, K, C, ep, frac):
     ids = random_ids(T, N, K, seed=T + N, invalid_frac=frac)
     for ep_rank in sorted({0, ep - 1}):
