@@ -195,6 +195,7 @@ struct GemmArgs {
   int64_t b_expert_stride;
   const int32_t *off;
   int E_L, M, N, Kdim;
+  int rows;         // buffer rows: offsets are clamped into [0, rows]
   const void *gu;   // DH: pre-activation [G U] rows (recomputed or saved), [rows, 2F]
   int F;
   void *Out;
@@ -217,11 +218,11 @@ __device__ __forceinline__ bool get_work(const GemmArgs &p, int tm, int tn, Work
     w.m0 = ((b / p.n_tiles_n) % p.m_tiles) * tm;
     w.n0 = (b % p.n_tiles_n) * tn;
     w.m_end = p.M;
-    w.kbeg = p.off[w.expert];
-    w.kend = p.off[w.expert + 1];
+    w.kbeg = min(max(p.off[w.expert], 0), p.rows);
+    w.kend = min(max(p.off[w.expert + 1], w.kbeg), p.rows);
     return true;
   } else {
-    const RowTile tl = find_row_tile(p.off, p.E_L, tm, p.n_tiles_n);
+    const RowTile tl = find_row_tile(p.off, p.E_L, tm, p.rows, p.n_tiles_n);
     if (!tl.valid) return false;
     w.expert = tl.expert;
     w.m0 = tl.row0;
@@ -952,6 +953,7 @@ int launch_expert_ffn_bwd_data_gu(const moe_shape_t &s, const int32_t *offsets, 
   GemmArgs p{};
   p.off = off;
   p.E_L = E_L;
+  p.rows = (int)buffer_rows(s);
   p.F = F;
   // dH = dY W_d (K = d, N = F), SwiGLU backward on [G U] in the epilogue -> [dG dU]
   p.A = dy; p.lda = d; p.B = w_down; p.ldb = F; p.b_expert_stride = (int64_t)d * F;
@@ -973,6 +975,7 @@ int launch_expert_ffn_bwd_weight(const moe_shape_t &s, const void *buf, const in
   GemmArgs p{};
   p.off = offsets + (size_t)s.ep_rank * (E_L + 1);
   p.E_L = E_L;
+  p.rows = (int)buffer_rows(s);
   p.F = F;
   // 4. dW_d[j] = dY^T H over the expert's rows (M = d, N = F), fp32
   p.A = dy; p.lda = d; p.B = h; p.ldb = F;

@@ -58,9 +58,9 @@ struct Tile {
 // workload among groups of 1, 2, 4 and 8 n-tiles and "all n-tiles of an
 // m-tile first").
 __device__ __forceinline__ Tile find_tile(const int32_t *__restrict__ off, int E_L, int bm,
-                                          int n_tiles_n) {
+                                          int rows, int n_tiles_n) {
   Tile tl;
-  const ExpertTile x = find_expert_tile(off, E_L, bm, n_tiles_n);
+  const ExpertTile x = find_expert_tile(off, E_L, bm, rows, n_tiles_n);
   tl.valid = x.valid;
   if (!x.valid) return tl;
   const int li = x.L - x.mstart * n_tiles_n;   // tile index inside the expert, < M * n_tiles_n
@@ -88,12 +88,12 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 template <bool GATE_UP>
 __global__ __launch_bounds__(256, 2) void k_gemm_bf16(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
-    const int32_t *__restrict__ off, uint16_t *__restrict__ Out, int E_L, int Kdim,
+    const int32_t *__restrict__ off, uint16_t *__restrict__ Out, int E_L, int rows, int Kdim,
     int Nout, int n_tiles_n) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kLds];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBW * kLds];
 
-  const Tile tl = find_tile(off, E_L, kBM, n_tiles_n);
+  const Tile tl = find_tile(off, E_L, kBM, rows, n_tiles_n);
   if (!tl.valid) return;
 
   const int tid = threadIdx.x;
@@ -491,7 +491,7 @@ template <bool GATE_UP, bool SAVE>
 __global__ __launch_bounds__(64 * BigTile::NW, 1) void k_gemm_bf16_big(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
     const int32_t *__restrict__ off, uint16_t *__restrict__ Out, uint16_t *__restrict__ GU,
-    int E_L, int Kdim, int Nout, int n_tiles_n) {
+    int E_L, int rows, int Kdim, int Nout, int n_tiles_n) {
   using P = BigTile;
   constexpr int BM = P::BM, BK = P::BK, NS = P::NS;
   // two A stages, NS = 3 B stages: the weight rows, which miss to HBM more
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(64 * BigTile::NW, 1) void k_gemm_bf16_big(
   __shared__ __attribute__((aligned(1024))) uint8_t smem[B_BASE + NS * P::B_BYTES];
 
   const uint32_t smem_l = lds_addr(smem);
-  const Tile tl = find_tile(off, E_L, BM, n_tiles_n);
+  const Tile tl = find_tile(off, E_L, BM, rows, n_tiles_n);
   if (!tl.valid) return;
 
   const int tid = threadIdx.x;
@@ -624,10 +624,10 @@ constexpr int kFM = 64, kFW = 64, kFK = 16;
 template <bool GATE_UP>
 __global__ __launch_bounds__(256) void k_gemm_f32(
     const float *__restrict__ A, const float *__restrict__ W, const int32_t *__restrict__ off,
-    float *__restrict__ Out, int E_L, int Kdim, int Nout, int n_tiles_n) {
+    float *__restrict__ Out, int E_L, int rows, int Kdim, int Nout, int n_tiles_n) {
   __shared__ float sA[kFK][kFM + 1];
   __shared__ float sB[kFK][kFW + 1];
-  const Tile tl = find_tile(off, E_L, kFM, n_tiles_n);
+  const Tile tl = find_tile(off, E_L, kFM, rows, n_tiles_n);
   if (!tl.valid) return;
   const int tid = threadIdx.x;
   const int ty = tid >> 4, tx = tid & 15;
@@ -704,20 +704,21 @@ template <bool GATE_UP>
 int launch_bf16(const moe_shape_t &s, const uint16_t *A, const uint16_t *W, const int32_t *off,
                 uint16_t *Out, int Kdim, int Nout, hipStream_t st, uint16_t *GU = nullptr) {
   const int E_L = s.N / s.ep_size;
+  const int rows = (int)buffer_rows(s);
   if (Kdim % 64 == 0) {
     using P = BigTile;
     const int ntn = (int)ceil_div(Nout, GATE_UP ? P::BW / 2 : P::BW);
     const dim3 grid(grid_blocks(s, P::BM, ntn)), block(64 * P::NW);
     if (GATE_UP && GU != nullptr)
       hipLaunchKernelGGL((k_gemm_bf16_big<true, true>), grid, block, 0, st, A, W, off, Out, GU,
-                         E_L, Kdim, Nout, ntn);
+                         E_L, rows, Kdim, Nout, ntn);
     else
       hipLaunchKernelGGL((k_gemm_bf16_big<GATE_UP, false>), grid, block, 0, st, A, W, off, Out,
-                         nullptr, E_L, Kdim, Nout, ntn);
+                         nullptr, E_L, rows, Kdim, Nout, ntn);
   } else {
     const int ntn = (int)ceil_div(Nout, GATE_UP ? kBW / 2 : kBW);
     hipLaunchKernelGGL(k_gemm_bf16<GATE_UP>, dim3(grid_blocks(s, kBM, ntn)), dim3(256), 0, st,
-                       A, W, off, Out, E_L, Kdim, Nout, ntn);
+                       A, W, off, Out, E_L, rows, Kdim, Nout, ntn);
   }
   return launch_status();
 }
@@ -741,7 +742,7 @@ int launch_expert_up(const moe_shape_t &s, const void *buf, const int32_t *offse
   const int ntn = (int)ceil_div(s.F, kFW / 2);
   hipLaunchKernelGGL(k_gemm_f32<true>, dim3(grid_blocks(s, kFM, ntn)), dim3(256), 0, st,
                      static_cast<const float *>(buf), static_cast<const float *>(w_gu), off,
-                     static_cast<float *>(h), E_L, s.d, s.F, ntn);
+                     static_cast<float *>(h), E_L, (int)buffer_rows(s), s.d, s.F, ntn);
   return launch_status();
 }
 
@@ -754,7 +755,7 @@ int launch_gemm_nt(const moe_shape_t &s, const void *A, const void *W, const int
   const int ntn = (int)ceil_div(Nout, kFW);
   hipLaunchKernelGGL(k_gemm_f32<false>, dim3(grid_blocks(s, kFM, ntn)), dim3(256), 0, st,
                      static_cast<const float *>(A), static_cast<const float *>(W), off,
-                     static_cast<float *>(Out), E_L, Kdim, Nout, ntn);
+                     static_cast<float *>(Out), E_L, (int)buffer_rows(s), Kdim, Nout, ntn);
   return launch_status();
 }
 
@@ -769,7 +770,7 @@ int launch_expert_down(const moe_shape_t &s, const void *h, const int32_t *offse
   const int ntn = (int)ceil_div(s.d, kFW);
   hipLaunchKernelGGL(k_gemm_f32<false>, dim3(grid_blocks(s, kFM, ntn)), dim3(256), 0, st,
                      static_cast<const float *>(h), static_cast<const float *>(w_d), off,
-                     static_cast<float *>(y), E_L, s.F, s.d, ntn);
+                     static_cast<float *>(y), E_L, (int)buffer_rows(s), s.F, s.d, ntn);
   return launch_status();
 }
 

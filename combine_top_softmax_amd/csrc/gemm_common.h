@@ -74,15 +74,17 @@ struct ExpertChunk {
   int o0, o1, mt, incl, tot;
 };
 
+// Offsets are clamped into the buffer, [0, rows], with o1 >= o0, so that
+// offsets from any source keep every tile inside the row buffers.
 __device__ __forceinline__ ExpertChunk expert_chunk(const int32_t *__restrict__ off, int E_L, int c,
-                                                    int bm) {
+                                                    int bm, int rows) {
   const int j = c + (threadIdx.x & 63);
   ExpertChunk ch;
   ch.o0 = 0;
   ch.o1 = 0;
   if (j < E_L) {
-    ch.o0 = off[j];
-    ch.o1 = off[j + 1];
+    ch.o0 = min(max(off[j], 0), rows);
+    ch.o1 = min(max(off[j + 1], ch.o0), rows);
   }
   ch.mt = (max(ch.o1 - ch.o0, 0) + bm - 1) / bm;
   ch.incl = wave_incl_scan_dpp(ch.mt);
@@ -113,24 +115,24 @@ struct ExpertTile {
 // m-tiles (bm rows each) of all local experts: the tile count is this times
 // the n-tiles. The c0 chunk (experts 0..63) is returned for reuse.
 __device__ __forceinline__ int count_m_tiles(const int32_t *__restrict__ off, int E_L, int bm,
-                                             ExpertChunk &c0) {
-  c0 = expert_chunk(off, E_L, 0, bm);
+                                             int rows, ExpertChunk &c0) {
+  c0 = expert_chunk(off, E_L, 0, bm, rows);
   int total_m = c0.tot;
-  for (int c = 64; c < E_L; c += 64) total_m += expert_chunk(off, E_L, c, bm).tot;
+  for (int c = 64; c < E_L; c += 64) total_m += expert_chunk(off, E_L, c, bm, rows).tot;
   return total_m;
 }
 
 // Tile L (< total) of the expert-by-expert numbering: its expert, the
 // expert's m-tile run and rows. c0: the first chunk, as count_m_tiles read it.
 __device__ __forceinline__ ExpertTile expert_tile_at(const int32_t *__restrict__ off, int E_L,
-                                                     int bm, int n_tiles_n, int L,
+                                                     int bm, int rows, int n_tiles_n, int L,
                                                      const ExpertChunk &c0) {
   ExpertTile t;
   t.valid = false;
   const int m_glob = L / n_tiles_n;
   int run = 0;
   for (int c = 0; c < E_L; c += 64) {
-    const ExpertChunk ch = (c == 0) ? c0 : expert_chunk(off, E_L, c, bm);
+    const ExpertChunk ch = (c == 0) ? c0 : expert_chunk(off, E_L, c, bm, rows);
     if (m_glob < run + ch.tot) {
       const uint64_t hit = __ballot(m_glob < run + ch.incl);
       if (hit == 0) return t;
@@ -153,16 +155,16 @@ __device__ __forceinline__ ExpertTile expert_tile_at(const int32_t *__restrict__
 }
 
 __device__ __forceinline__ ExpertTile find_expert_tile(const int32_t *__restrict__ off, int E_L,
-                                                       int bm, int n_tiles_n) {
+                                                       int bm, int rows, int n_tiles_n) {
   ExpertTile t;
   t.valid = false;
   ExpertChunk c0;
-  const int total = count_m_tiles(off, E_L, bm, c0) * n_tiles_n;
+  const int total = count_m_tiles(off, E_L, bm, rows, c0) * n_tiles_n;
   const int q = (total + kNumXcd - 1) / kNumXcd;
   const int slot = blockIdx.x / kNumXcd;
   const int L = (blockIdx.x % kNumXcd) * q + slot;
   if (slot >= q || L >= total) return t;
-  return expert_tile_at(off, E_L, bm, n_tiles_n, L, c0);
+  return expert_tile_at(off, E_L, bm, rows, n_tiles_n, L, c0);
 }
 
 // Row-mode tiles: m-tile by m-tile, its n_tiles_n n-tiles consecutive.
@@ -172,9 +174,9 @@ struct RowTile {
 };
 
 __device__ __forceinline__ RowTile find_row_tile(const int32_t *__restrict__ off, int E_L, int tm,
-                                                 int n_tiles_n) {
+                                                 int rows, int n_tiles_n) {
   RowTile tl;
-  const ExpertTile x = find_expert_tile(off, E_L, tm, n_tiles_n);
+  const ExpertTile x = find_expert_tile(off, E_L, tm, rows, n_tiles_n);
   tl.valid = x.valid;
   if (!x.valid) return tl;
   const int m_glob = x.L / n_tiles_n;

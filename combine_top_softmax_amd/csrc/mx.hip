@@ -289,10 +289,10 @@ template <bool GATE_UP>
 __global__ __launch_bounds__(mxg::NT, 1) void k_gemm_mx(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ W,
     const uint8_t *__restrict__ Ws, const int32_t *__restrict__ off, uint8_t *__restrict__ OutQ,
-    uint8_t *__restrict__ OutS, uint16_t *__restrict__ OutY, int E_L, int Kdim, int Nout,
-    int n_tiles_n) {
+    uint8_t *__restrict__ OutS, uint16_t *__restrict__ OutY, int E_L, int rows, int Kdim,
+    int Nout, int n_tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * mxg::STAGE];
-  RowTile tl = find_row_tile(off, E_L, mxg::BM, n_tiles_n);
+  RowTile tl = find_row_tile(off, E_L, mxg::BM, rows, n_tiles_n);
   if (!tl.valid) return;
   // wave-uniform: keep the tile in scalar registers (scalar load bases)
   tl.expert = __builtin_amdgcn_readfirstlane(tl.expert);
@@ -530,7 +530,8 @@ int launch_expert_up_mx(const moe_shape_t &s, const uint8_t *qbuf, const uint8_t
   const int32_t *off = offsets + (size_t)s.ep_rank * (E_L + 1);
   const int ntn = (int)ceil_div(s.F, mxg::BW / 2);
   hipLaunchKernelGGL(k_gemm_mx<true>, dim3(mx_grid(s, ntn)), dim3(mxg::NT), 0, st, qbuf, sbuf,
-                     w_gu_q, w_gu_s, off, h_q, h_s, nullptr, E_L, s.d, s.F, ntn);
+                     w_gu_q, w_gu_s, off, h_q, h_s, nullptr, E_L, (int)buffer_rows(s), s.d, s.F,
+                     ntn);
   return launch_status();
 }
 
@@ -541,8 +542,8 @@ int launch_expert_down_mx(const moe_shape_t &s, const uint8_t *h_q, const uint8_
   const int32_t *off = offsets + (size_t)s.ep_rank * (E_L + 1);
   const int ntn = (int)ceil_div(s.d, mxg::BW);
   hipLaunchKernelGGL(k_gemm_mx<false>, dim3(mx_grid(s, ntn)), dim3(mxg::NT), 0, st, h_q, h_s,
-                     w_d_q, w_d_s, off, nullptr, nullptr, static_cast<uint16_t *>(y), E_L, s.F,
-                     s.d, ntn);
+                     w_d_q, w_d_s, off, nullptr, nullptr, static_cast<uint16_t *>(y), E_L,
+                     (int)buffer_rows(s), s.F, s.d, ntn);
   return launch_status();
 }
 
