@@ -379,3 +379,48 @@ def test_row_calls_skip_rows_outside_the_buffer():
     rq, rs, written = orc.dispatch_mx(to_np(inp.x), m_rank, row_np, ep, R)
     np.testing.assert_array_equal(to_np(qbuf)[written], rq[written])
     np.testing.assert_array_equal(to_np(sbuf)[written][:, :d // 32], rs[written])
+
+
+def test_expert_gemms_clamp_offsets_into_the_buffer():
+    """Offsets from elsewhere that start below row 0 and end past Rmax: the
+    grouped GEMMs (forward up/down and the weight gradients) clamp them into
+    [0, Rmax], so the results equal those of the clamped offsets and nothing
+    outside the row buffers is touched. Every buffer is a view with 128 guard
+    rows on either side (more than the offsets overshoot), so even an
+    unclamped access would stay inside the allocation."""
+    cfg = LayerConfig("offsets_outside", T=300, d=128, N=4, K=2, F=128, cf=Fraction(1),
+                      dtype="bf16", seed=44)
+    shape = moe.MoeShape.from_config(cfg)
+    R, d, F, G = shape.rows, cfg.d, cfg.F, 128
+    inp = make_inputs(cfg, "cuda")
+    gen = torch.Generator(device="cuda").manual_seed(6)
+
+    def data(cols, dtype=torch.bfloat16):       # random rows, guards included
+        big = torch.randn(R + 2 * G, cols, generator=gen, device="cuda").to(dtype)
+        return big, big[G:G + R]
+
+    def poisoned(cols):
+        big = poison_(torch.empty(R + 2 * G, cols, dtype=torch.bfloat16, device="cuda"))
+        return big, big[G:G + R]
+
+    bad = torch.tensor([[-50, 50, 120, R - 10, R + 100]], dtype=torch.int32, device="cuda")
+    good = torch.tensor([[0, 50, 120, R - 10, R]], dtype=torch.int32, device="cuda")
+    _, buf = data(d)
+    _, dy = data(d)
+    _, dgu = data(2 * F)
+    res = {}
+    for name, off in (("bad", bad), ("good", good)):
+        big_h, h = poisoned(F)
+        big_y, y = poisoned(d)
+        moe.moe_expert_ffn(shape, buf, off, inp.w_gu, inp.w_d, h, y)
+        dw_gu = torch.empty(cfg.N, 2 * F, d, device="cuda")
+        dw_down = torch.empty(cfg.N, d, F, device="cuda")
+        moe.moe_expert_ffn_bwd_weight(shape, buf, off, h, dy, dgu, dw_gu, dw_down)
+        torch.cuda.synchronize()
+        res[name] = (big_h, big_y, dw_gu, dw_down)
+    big_h, big_y = res["bad"][0], res["bad"][1]
+    for big in (big_h, big_y):
+        assert bool(is_poison(big[:G]).all()) and bool(is_poison(big[G + R:]).all())
+    for a, b in zip(res["bad"], res["good"]):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
