@@ -21,12 +21,17 @@
  *     never allocates and keeps no state between calls (Olmo-core MoE report,
  *     Sec. 08 "Synchronization-Free Training", Sec. 8.5: route metadata stays
  *     on the device; capacity-shaped buffers are fixed before the loop).
+ *     The one exception is moe_route_noalloc, whose scratch is a static
+ *     device array whose address is looked up once per device.
  *   - Only host arguments are validated. Return value 0 = success, otherwise
  *     one of the negative MOE_E* codes below; nothing is enqueued on error.
  *   - Device-data preconditions that are NOT checked (checking would need a
  *     device-to-host read): moe_route_map ids lie in
  *     [-1, N) and the valid ids of one token are distinct; buf, h, y and out
- *     do not alias each other or the inputs.
+ *     do not alias each other or the inputs. Route maps and offsets that
+ *     reach the row calls and the GEMMs are bounded on the device instead:
+ *     rows outside [0, Rmax) are skipped and offsets are clamped into
+ *     [0, Rmax] (see moe_route_out_t and moe_expert_ffn).
  *   - Expert placement is contiguous: rank r owns global experts
  *     [r*E_L, (r+1)*E_L), E_L = N / ep_size; this GPU is rank ep_rank and
  *     holds only its E_L experts (AWS Neuron vLLM "Expert Parallelism (EP)"
@@ -195,7 +200,11 @@ int moe_dispatch_rows(const moe_shape_t *shape, const void *x, const int32_t *de
  * buf [Rmax, d], w_gu [E_L, 2F, d] (rows 0..F-1 gate, F..2F-1 up),
  * w_down [E_L, d, F], h [Rmax, F] (caller-owned scratch), y [Rmax, d];
  * all in dtype. Accumulation is fp32; H and Y are stored in dtype with
- * round-to-nearest-even. Only prefix rows of h and y are written. */
+ * round-to-nearest-even. Only prefix rows of h and y are written.
+ * Every grouped GEMM here and below (forward, backward, MXFP8) reads each
+ * expert's range as [min(max(o_j,0),Rmax), min(max(o_{j+1},start),Rmax)),
+ * so offsets from any source keep it inside the row buffers; offsets that
+ * are not non-decreasing give overlapping experts and unspecified values. */
 int moe_expert_ffn(const moe_shape_t *shape, const void *buf, const int32_t *offsets,
                    const void *w_gu, const void *w_down, void *h, void *y,
                    hipStream_t stream);
