@@ -25,3 +25,11 @@ def test_committed_traffic_profile_matches_the_gemm_code():
     t = bench.traffic_from_profile("zipf_skew_bf16", "up")
     assert t is not None and t > 0
     assert bench.traffic_from_profile("no_such_workload", "up") is None
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
