@@ -81,6 +81,22 @@ def traffic_from_profile(workload: str, kernel: str):
         return None
 
 
+def _host_cpu() -> dict:
+    """The host the oracle ran on: logical CPUs visible to this process and the
+    CPU model (from /proc/cpuinfo)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"logical_cpus_visible": n, "cpu_model": model}
+
+
 def cpu_baseline(cfg, target_s: float) -> dict:
     """The oracle, as it stands, on a bounded sample of the same workload: a
     T_s-token layer of the same shape drawn with the same recipe (capacity
@@ -112,6 +128,7 @@ def cpu_baseline(cfg, target_s: float) -> dict:
         rows, dt, n = run(T_s, repeats=max(1, min(5, int(target_s / max(dt, 1e-3)))))
     threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
     return {"value": rows / dt, "unit": "token-rows/s", "cores": int(threads), "kind": "oracle",
+            "host": _host_cpu(),
             "sample": f"whole layer (route, dispatch, FFN, combine) on a {T_s}-token layer of "
                       f"the {cfg.name} shape, same input recipe, capacity recomputed for {T_s} "
                       f"tokens: {rows} routed rows in {dt:.2f} s (median of {n} runs); "

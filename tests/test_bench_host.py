@@ -33,3 +33,9 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_host_cpu_record_names_the_cpus_seen():
+    h = bench._host_cpu()
+    assert h["logical_cpus_visible"] >= 1
+    assert h["cpu_model"] is None or isinstance(h["cpu_model"], str)
